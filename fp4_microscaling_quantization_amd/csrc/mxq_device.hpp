@@ -1,0 +1,290 @@
+// Device building blocks of the fused rotate + quantize kernels (gfx950).
+//
+// Work layout: a 32-element MX block is spread over 4 lanes ("a quad" of the
+// block), 8 consecutive block positions per lane; lane `pos` (0..3) holds
+// positions 8*pos .. 8*pos+7.  The 4 lanes of a block sit in one 16-lane DPP
+// row, at lane distances given by the template arguments XA (partner holding
+// the other half of a 16-position half-block: pos ^ 1) and XB (the other
+// 16-position half: pos ^ 2).  All cross-lane traffic is DPP (full-rate VALU).
+//
+// Method sources (web pages): MX blocks of 32 with one E8M0 exponent set by
+// the largest exponent in the block -- htx.com news on "Pretraining large
+// language models with MXFP4", section "Que es MXFP4?"; H16/H32 rotations --
+// gist.science summary "Pre-treinamento de Modelos de Linguagem Grandes com
+// MXFP4", section "Metodologia"; Hadamard after random sign inversion and
+// stochastic rounding -- the htx.com news, section "Experimento de
+// diagnostico"; RTNE onto E2M1 and the uniform E1M2 grid, SR only on dY --
+// gist.science summary "Repensando o Vies de Encolhimento (Shrinkage Bias) no
+// Pre-treinamento de LLMs em FP4", sections "Metodologia 1" and "2".
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+enum : int { kE2M1 = 0, kE1M2 = 1 };
+enum : int { kRTNE = 0, kSR = 1 };
+
+// Runtime knobs handed to every quantize kernel.
+struct QKnobs {
+    uint32_t sign_mask;
+    uint32_t seed_lo, seed_hi;
+    uint32_t stream;
+    uint32_t sr_bits;  // 8 or 16
+};
+
+__device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
+
+// ---- lane exchange within a 16-lane DPP row: returns the value of lane ^ X --
+template <int X> __device__ __forceinline__ uint32_t lane_xor(uint32_t v);
+template <> __device__ __forceinline__ uint32_t lane_xor<1>(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+}
+template <> __device__ __forceinline__ uint32_t lane_xor<2>(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+}
+template <> __device__ __forceinline__ uint32_t lane_xor<4>(uint32_t v)
+{
+    // banks 0 and 2 read lane+4 (row_shl:4), banks 1 and 3 read lane-4 (row_shr:4)
+    int t = __builtin_amdgcn_update_dpp((int)v, (int)v, 0x104, 0xF, 0x5, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)v, 0x114, 0xF, 0xA, false);
+}
+template <> __device__ __forceinline__ uint32_t lane_xor<8>(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+}
+template <int X> __device__ __forceinline__ float lane_xor_f(float v)
+{
+    return as_f(lane_xor<X>(as_u(v)));
+}
+
+// ---- Philox4x32-10 (Salmon et al., SC'11) -----------------------------------
+struct Rand4 {
+    uint32_t w[4];
+};
+__device__ __forceinline__ Rand4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1)
+{
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    Rand4 r;
+    r.w[0] = c0; r.w[1] = c1; r.w[2] = c2; r.w[3] = c3;
+    return r;
+}
+
+// Random bits of the 8 positions 8*pos .. 8*pos+7 of block `blk`.
+__device__ __forceinline__ void sr_bits8(const QKnobs &kn, int pos, uint64_t blk, uint32_t (&r)[8])
+{
+    const uint32_t blo = (uint32_t)blk, bhi = (uint32_t)(blk >> 32);
+    if (kn.sr_bits == 16) {
+        // counter word 0 = j >> 3 = pos; element i uses half (i&1) of word i>>1
+        Rand4 q = philox4x32_10((uint32_t)pos, blo, bhi, kn.stream, kn.seed_lo, kn.seed_hi);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r[i] = (q.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
+    } else {
+        // counter word 0 = j >> 4 = pos >> 1; element j = 8 pos + i uses byte
+        // (j & 3) of word ((j >> 2) & 3) = 2 (pos & 1) + (i >> 2)
+        Rand4 q = philox4x32_10((uint32_t)(pos >> 1), blo, bhi, kn.stream, kn.seed_lo, kn.seed_hi);
+        const uint32_t wa = (pos & 1) ? q.w[2] : q.w[0];
+        const uint32_t wb = (pos & 1) ? q.w[3] : q.w[1];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            r[i] = (((i < 4) ? wa : wb) >> (8 * (i & 3))) & 0xFFu;
+    }
+}
+
+// ---- rounding of a normalized magnitude a = |y| 2^-e (0 <= a < 2^(emax+1)) --
+// E1M2 levels 0.5 m: m = RNE(2a) by one fused multiply-add against 2^23
+// (single rounding of the exact 2a), saturated at 7.
+__device__ __forceinline__ uint32_t rtne_e1m2(float a)
+{
+    const float t = __builtin_fmaf(a, 2.0f, 8388608.0f);
+    return min(as_u(t) - 0x4B000000u, 7u);
+}
+
+// E2M1 segment of a: 0 for a < 2 (step 0.5), 1 for [2, 4) (step 1), 2 for
+// a >= 4 (step 2); from the fp32 exponent field.
+__device__ __forceinline__ int e2m1_segment(float a)
+{
+    return min(max((int)(as_u(a) >> 23) - 127, 0), 2);
+}
+
+// E2M1 in software: RNE(a / step) + segment offset, saturated at 7.
+__device__ __forceinline__ uint32_t rtne_e2m1_soft(float a)
+{
+    const int d = e2m1_segment(a);
+    const float s = as_f((uint32_t)(128 - d) << 23);          // 2^(1-d) = 1/step
+    const float t = __builtin_fmaf(a, s, 8388608.0f);          // a*s exact
+    return min(as_u(t) - 0x4B000000u + 2u * (uint32_t)d, 7u);
+}
+
+// SR: round up iff 2r + 1 < p 2^(B+1), p the exact fraction of the gap.
+__device__ __forceinline__ uint32_t sr_e1m2(float a, uint32_t r, float two_pow_b1)
+{
+    const float x = a * 2.0f;
+    const float k = floorf(x);
+    const float p = x - k;                                     // exact
+    const uint32_t up = (float)(2u * r + 1u) < p * two_pow_b1;
+    return min((uint32_t)k + up, 7u);
+}
+__device__ __forceinline__ uint32_t sr_e2m1(float a, uint32_t r, float two_pow_b1)
+{
+    const int d = e2m1_segment(a);
+    const float x = a * as_f((uint32_t)(128 - d) << 23);       // a / step, exact
+    const float k = floorf(x);
+    const float p = x - k;
+    const uint32_t up = (float)(2u * r + 1u) < p * two_pow_b1;
+    return min((uint32_t)k + 2u * (uint32_t)d + up, 7u);
+}
+
+// ---- block rotation of the lane's 8 values -----------------------------------
+// y = fl32(1/sqrt(n)) * H_n * v on each n-position sub-block, H_n Sylvester,
+// butterfly stages of stride 1, 2, 4 (in-lane), 8 (lane ^ XA) and, for n = 32,
+// 16 (lane ^ XB) -- the same fp32 operations in the same stage order as the
+// fast transform applied to the whole block.
+template <int HN, int XA, int XB>
+__device__ __forceinline__ void rotate8(float (&v)[8], int pos)
+{
+    if constexpr (HN >= 16) {
+        // Butterfly stages of stride 1, 2, 4 inside the lane ...
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (!(i & h)) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+            }
+        }
+        // ... stride 8 across the pair (pos, pos^1): the lower lane keeps
+        // u + u', the upper one u' - u (own value negated, then added).
+        {
+            const uint32_t neg = (pos & 1) ? 0x80000000u : 0u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = lane_xor_f<XA>(v[i]);
+                v[i] = p + as_f(as_u(v[i]) ^ neg);
+            }
+        }
+        if constexpr (HN == 32) {
+            const uint32_t neg = (pos & 2) ? 0x80000000u : 0u;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float p = lane_xor_f<XB>(v[i]);
+                v[i] = p + as_f(as_u(v[i]) ^ neg);
+            }
+        }
+        const float c = HN == 16 ? 0.25f : as_f(0x3E3504F3u);  // fl32(1/sqrt(n))
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            v[i] = v[i] * c;
+    }
+}
+
+// ---- rounding of 8 signed values y * inv onto the grid --------------------
+// Returns the sign-magnitude nibbles, element i in bits 4i..4i+3.  `r` and
+// `tpb` = 2^(B+1) are only read for SR.
+template <int GRID, int ROUND>
+__device__ __forceinline__ uint32_t round8(const float (&v)[8], float inv, const uint32_t (&r)[8],
+                                           float tpb)
+{
+    uint32_t w = 0;
+    if constexpr (GRID == kE2M1 && ROUND == kRTNE) {
+        // the gfx950 FP4 convert rounds to nearest-even E2M1 with saturation
+        // and keeps the sign (including -0); y * 2^-e is exact
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * inv, v[1] * inv, 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * inv, v[3] * inv, 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * inv, v[5] * inv, 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * inv, v[7] * inv, 1.0f, 3);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float a = fabsf(v[i]) * inv;
+            uint32_t m;
+            if constexpr (ROUND == kRTNE)
+                m = GRID == kE1M2 ? rtne_e1m2(a) : rtne_e2m1_soft(a);
+            else
+                m = GRID == kE1M2 ? sr_e1m2(a, r[i], tpb) : sr_e2m1(a, r[i], tpb);
+            w |= (m | ((as_u(v[i]) >> 28) & 8u)) << (4 * i);
+        }
+    }
+    return w;
+}
+
+// ---- the 8-element slice of one block ---------------------------------------
+// v: this lane's 8 values (bf16 already widened, sign mask already applied).
+// Returns the 8 sign-magnitude nibbles packed little-endian (position 8*pos+i
+// in bits 4i..4i+3); *scale receives the block's E8M0 code (all 4 lanes).
+template <int GRID, int ROUND, int HN, int XA, int XB>
+__device__ __forceinline__ uint32_t quant8(float (&v)[8], int pos, uint64_t blk, const QKnobs &kn,
+                                           uint32_t *scale)
+{
+    constexpr int EMAX = GRID == kE2M1 ? 2 : 1;
+    rotate8<HN, XA, XB>(v, pos);
+    // Block maximum of |y| as an unsigned compare of the magnitude bits: NaN
+    // patterns exceed Inf, which exceeds every finite value.
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
+    am = max(am, lane_xor<XA>(am));
+    am = max(am, lane_xor<XB>(am));
+    // e = floor(log2 amax) - EMAX, clamped at -127; code e + 127.  For a
+    // normal amax floor(log2) is its biased exponent - 127; a zero or
+    // subnormal amax gives e <= -127 - EMAX, i.e. code 0.
+    const uint32_t sc = am >= 0x7F800000u ? 0xFFu : (uint32_t)max((int)(am >> 23) - EMAX, 0);
+    *scale = sc;
+    const float inv = as_f((254u - min(sc, 253u)) << 23);      // 2^-e, exact
+
+    uint32_t r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float tpb = 0.f;
+    if constexpr (ROUND == kSR) {
+        sr_bits8(kn, pos, blk, r);
+        tpb = kn.sr_bits == 16 ? 131072.0f : 512.0f;           // 2^(B+1)
+    }
+    const uint32_t w = round8<GRID, ROUND>(v, inv, r, tpb);
+    return sc == 0xFFu ? 0u : w;
+}
+
+// FP6 E2M3 code of a nibble (value-preserving): E2M1 level m is E2M3 code
+// 4m; E1M2 level 0.5 m is 4m below 2 and 2m + 8 from 2 up.  Sign to bit 5.
+template <int GRID>
+__device__ __forceinline__ uint32_t e2m3_of_nibble(uint32_t nib)
+{
+    const uint32_t m = nib & 7u, s = (nib & 8u) << 2;
+    if constexpr (GRID == kE2M1)
+        return s | (m << 2);
+    else
+        return s | (m < 4u ? (m << 2) : (2u * m + 8u));
+}
+
+// Pack 8 nibbles into 8 E2M3 codes: 48 bits, element i at bits 6i.
+template <int GRID>
+__device__ __forceinline__ uint64_t e2m3_pack8(uint32_t w)
+{
+    uint64_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc |= (uint64_t)e2m3_of_nibble<GRID>((w >> (4 * i)) & 15u) << (6 * i);
+    return acc;
+}
+
+}  // namespace mxq

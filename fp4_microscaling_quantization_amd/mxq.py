@@ -1,0 +1,214 @@
+"""Thin ctypes binding of libmxq (include/mxq.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libmxq.so.  PyTorch supplies device memory and the current stream.
+Loading fails loudly when the library has not been built; there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmxq.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_DEVICE, ERR_WORKSPACE = range(7)
+GRID_E2M1, GRID_E1M2 = 0, 1
+RTNE, SR = 0, 1
+FMT_FP4, FMT_E2M3 = 0, 1
+AXIS_ROW, AXIS_COL = 0, 1
+OUT_F32, OUT_BF16 = 0, 1
+
+SYMBOLS = ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_bias_stats",
+           "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_status_string",
+           "mxq_abi_version")
+
+
+class QConfig(C.Structure):
+    _fields_ = [("grid", C.c_int32), ("round", C.c_int32), ("hadamard_n", C.c_int32),
+                ("sign_mask", C.c_uint32), ("sr_seed", C.c_uint64), ("sr_stream", C.c_uint32),
+                ("sr_bits", C.c_uint32)]
+
+
+class QTensor(C.Structure):
+    _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("fmt", C.c_int32),
+                ("grid", C.c_int32)]
+
+
+class Stats(C.Structure):
+    _fields_ = [("sum_abs_y", C.c_double), ("sum_signed_err", C.c_double),
+                ("sum_y2", C.c_double), ("sum_err2", C.c_double), ("sum_err_norm", C.c_double),
+                ("sum_err_norm_sat", C.c_double), ("level_err_norm", C.c_double * 8),
+                ("n", C.c_uint64), ("n_saturated", C.c_uint64),
+                ("n_nonfinite_blocks", C.c_uint64), ("level_count", C.c_uint64 * 8)]
+
+
+class MxqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libmxq.so is not built ({LIB_PATH}); run "
+                              "`python -c 'import __graft_entry__ as g; g.build()'` first")
+        L = C.CDLL(LIB_PATH)
+        P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        L.mxq_quantize.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, C.POINTER(QTensor),
+                                   C.POINTER(QTensor), P]
+        L.mxq_dequantize.argtypes = [C.POINTER(QTensor), i64, i64, i32, P, i64, P]
+        L.mxq_wgrad_gemm.argtypes = [C.POINTER(QTensor), C.POINTER(QTensor), i64, i64, i64, P,
+                                     i64, P]
+        L.mxq_bias_stats.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, i32, C.POINTER(QTensor),
+                                     P, P, C.c_size_t, P]
+        L.mxq_bias_stats_workspace_size.argtypes = [i64, i64, i32]
+        L.mxq_bias_stats_workspace_size.restype = C.c_size_t
+        L.mxq_round_to_grid.argtypes = [i32, i32, i32, P, P, i64, P, P]
+        L.mxq_status_string.argtypes = [i32]
+        L.mxq_status_string.restype = C.c_char_p
+        L.mxq_abi_version.restype = i32
+        for name in ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_bias_stats",
+                     "mxq_round_to_grid"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().mxq_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise MxqError(fn, status)
+
+
+def _ptr(t) -> C.c_void_p | None:
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def qconfig(grid=GRID_E2M1, round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
+            sr_bits=16) -> QConfig:
+    return QConfig(grid, round, hadamard_n, sign_mask & 0xFFFFFFFF, sr_seed, sr_stream, sr_bits)
+
+
+def block_bytes(fmt: int) -> int:
+    return 16 if fmt == FMT_FP4 else 24
+
+
+def empty_qtensor(lines: int, k: int, fmt: int, device):
+    """Device buffers for a [lines x k] block-quantized tensor: (codes, scales)."""
+    import torch
+    nb = k // 32
+    codes = torch.empty((lines, nb * block_bytes(fmt)), dtype=torch.uint8, device=device)
+    scales = torch.empty((lines, nb), dtype=torch.uint8, device=device)
+    return codes, scales
+
+
+def qtensor(codes, scales, fmt: int, grid: int) -> QTensor:
+    return QTensor(codes.data_ptr(), scales.data_ptr(), fmt, grid)
+
+
+# ---- entry points ---------------------------------------------------------
+
+def quantize_into(cfg: QConfig, x, row=None, col=None, rows=None, cols=None, ld=None,
+                  stream=None):
+    """mxq_quantize on caller-owned buffers.  row/col: (codes, scales, fmt) or None."""
+    rows = x.shape[0] if rows is None else rows
+    cols = x.shape[1] if cols is None else cols
+    ld = x.stride(0) if ld is None else ld
+    rt = QTensor(row[0].data_ptr(), row[1].data_ptr(), row[2], cfg.grid) if row else None
+    ct = QTensor(col[0].data_ptr(), col[1].data_ptr(), col[2], cfg.grid) if col else None
+    st = lib().mxq_quantize(C.byref(cfg), _ptr(x), rows, cols, ld,
+                            C.byref(rt) if rt else None, C.byref(ct) if ct else None,
+                            _stream(stream))
+    _check("mxq_quantize", st)
+
+
+def quantize(x, grid=GRID_E2M1, round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
+             sr_bits=16, row=True, col=False, row_fmt=FMT_FP4, col_fmt=FMT_FP4, stream=None):
+    """Quantize a 2-D bf16 CUDA tensor; returns {'row': (codes, scales), 'col': (...)}."""
+    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits)
+    rows, cols = x.shape
+    out = {}
+    r = c = None
+    if row:
+        rc, rs = empty_qtensor(rows, cols, row_fmt, x.device)
+        r = (rc, rs, row_fmt)
+        out["row"] = (rc, rs)
+    if col:
+        cc, cs = empty_qtensor(cols, rows, col_fmt, x.device)
+        c = (cc, cs, col_fmt)
+        out["col"] = (cc, cs)
+    quantize_into(cfg, x, r, c, stream=stream)
+    return out
+
+
+def dequantize(codes, scales, fmt: int, grid: int, out_dtype=OUT_F32, stream=None):
+    import torch
+    lines = scales.shape[0]
+    k = scales.shape[1] * 32
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    out = torch.empty((lines, k), dtype=dt, device=codes.device)
+    q = qtensor(codes, scales, fmt, grid)
+    _check("mxq_dequantize", lib().mxq_dequantize(C.byref(q), lines, k, out_dtype, _ptr(out), k,
+                                                  _stream(stream)))
+    return out
+
+
+def wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid, out=None,
+               stream=None):
+    """C [m x n] fp32 = A [m x k] B [n x k]^T on block-quantized operands."""
+    import torch
+    m, n = a_scales.shape[0], b_scales.shape[0]
+    k = a_scales.shape[1] * 32
+    assert b_scales.shape[1] * 32 == k
+    c = torch.empty((m, n), dtype=torch.float32, device=a_codes.device) if out is None else out
+    qa = qtensor(a_codes, a_scales, a_fmt, a_grid)
+    qb = qtensor(b_codes, b_scales, b_fmt, b_grid)
+    _check("mxq_wgrad_gemm", lib().mxq_wgrad_gemm(C.byref(qa), C.byref(qb), m, n, k, _ptr(c),
+                                                  c.stride(0), _stream(stream)))
+    return c
+
+
+def bias_stats(x, axis: int, codes, scales, fmt: int, grid=GRID_E2M1, round=RTNE, hadamard_n=0,
+               sign_mask=0, sr_seed=0, sr_stream=0, sr_bits=16, stream=None) -> dict:
+    import torch
+    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits)
+    rows, cols = x.shape
+    wsb = lib().mxq_bias_stats_workspace_size(rows, cols, axis)
+    ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device=x.device)
+    out = torch.zeros(C.sizeof(Stats), dtype=torch.uint8, device=x.device)
+    q = qtensor(codes, scales, fmt, grid)
+    _check("mxq_bias_stats", lib().mxq_bias_stats(C.byref(cfg), _ptr(x), rows, cols, x.stride(0),
+                                                  axis, C.byref(q), _ptr(out), _ptr(ws), wsb,
+                                                  _stream(stream)))
+    raw = bytes(out.cpu().numpy().tobytes())
+    st = Stats.from_buffer_copy(raw)
+    d = {k: getattr(st, k) for k, _ in Stats._fields_}
+    d["level_err_norm"] = list(st.level_err_norm)
+    d["level_count"] = list(st.level_count)
+    return d
+
+
+def round_to_grid(a, grid: int, round=RTNE, rand=None, sr_bits=16, out=None, stream=None):
+    """Nibble of each fp32 value of `a` (already divided by its block scale)."""
+    import torch
+    n = a.numel()
+    codes = torch.empty(n, dtype=torch.uint8, device=a.device) if out is None else out
+    _check("mxq_round_to_grid", lib().mxq_round_to_grid(grid, round, sr_bits, _ptr(a), _ptr(rand),
+                                                        n, _ptr(codes), _stream(stream)))
+    return codes

@@ -1,0 +1,202 @@
+/*
+ * mxq.h -- C ABI of libmxq: MX block-32 FP4 quantization with a block
+ * Hadamard rotation, and the block-scaled FP4 weight-gradient GEMM, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method follows four web pages:
+ *  - htx.com (es-es) news on "Pretraining large language models with MXFP4 on
+ *    Native FP4 Hardware" (arXiv 2605.09825): section "Que es MXFP4?" (blocks
+ *    of 32 elements with one shared E8M0 exponent, the block's largest
+ *    exponent; 4-bit float elements) and section "Experimento de diagnostico"
+ *    (the Fprop / Dgrad / Wgrad GEMMs Y = X W^T, dX = dY W, dW = dY^T X;
+ *    stochastic rounding; Hadamard transform after random sign inversion).
+ *  - gist.science (pt) summary "Pre-treinamento de Modelos de Linguagem
+ *    Grandes com MXFP4": section "Metodologia" (deterministic H16 and H32
+ *    rotations).
+ *  - gist.science (pt, ko) summary "Repensando o Vies de Encolhimento
+ *    (Shrinkage Bias) no Pre-treinamento de LLMs em FP4": "Metodologia 1"
+ *    (RTNE on the non-uniform E2M1 grid and its shrinkage bias (l_i - r_i)/2),
+ *    "Metodologia 2" (the uniform E1M2 / INT4-style grid; SR only on dY),
+ *    "Resultados Experimentais" (SQNR diagnostics) and "Eficiencia" (fused
+ *    rotation + quantization).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no mutable global state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    Work is enqueued asynchronously; nothing is synchronized.
+ *  - Arguments are validated on the host before any launch; on failure the
+ *    call returns a non-zero mxq_status and has no side effect.  A failed
+ *    launch returns MXQ_ERR_DEVICE.  Faults inside kernels surface at the
+ *    caller's next synchronization.  Nothing is printed.
+ *  - Calls are thread-safe; calls that write the same output race.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+typedef int32_t mxq_status;
+#define MXQ_OK 0
+#define MXQ_ERR_NULL 1          /* a required pointer is NULL                 */
+#define MXQ_ERR_SHAPE 2         /* a size is negative / not a multiple of 32  */
+#define MXQ_ERR_ALIGN 3         /* a pointer or leading dimension misaligned  */
+#define MXQ_ERR_UNSUPPORTED 4   /* an enum value or combination not supported */
+#define MXQ_ERR_DEVICE 5        /* the HIP launch failed                      */
+#define MXQ_ERR_WORKSPACE 6     /* the workspace is missing or too small      */
+
+/* Element grids (the 3-bit magnitude m of a sign-magnitude nibble s<<3|m):
+ *   MXQ_GRID_E2M1: m -> {0, 0.5, 1, 1.5, 2, 3, 4, 6}; top-level exponent emax 2.
+ *   MXQ_GRID_E1M2: m -> 0.5*m = {0, 0.5, ..., 3.5} (uniform); emax 1. */
+#define MXQ_GRID_E2M1 0
+#define MXQ_GRID_E1M2 1
+
+/* Rounding of the normalized magnitude a = |y| / 2^e onto the grid:
+ *   MXQ_ROUND_RTNE: nearest level, ties to the even code, saturating.
+ *   MXQ_ROUND_SR:   between the neighbouring levels q_k <= a < q_(k+1), round
+ *                   up iff r + 1/2 < p * 2^B with p = (a - q_k)/(q_(k+1) - q_k)
+ *                   and r the element's B random bits (below); a at or above
+ *                   the top level stays at the top level. */
+#define MXQ_ROUND_RTNE 0
+#define MXQ_ROUND_SR 1
+
+/* Code storage of one 32-element block:
+ *   MXQ_FMT_FP4:  16 bytes; byte j = nibble(2j) | nibble(2j+1) << 4.
+ *   MXQ_FMT_E2M3: 24 bytes; element i is the OCP FP6 E2M3 code (sign in bit 5)
+ *                 of the same value, at bits 6i..6i+5 of the little-endian
+ *                 192-bit block.  Lossless for both grids; it is the operand
+ *                 form the FP6 matrix cores read (E1M2 levels are not E2M1). */
+#define MXQ_FMT_FP4 0
+#define MXQ_FMT_E2M3 1
+
+#define MXQ_AXIS_ROW 0          /* blocks run along the last (contiguous) dim */
+#define MXQ_AXIS_COL 1          /* blocks run along the first dim; transposed */
+
+#define MXQ_OUT_F32 0
+#define MXQ_OUT_BF16 1
+
+/* Quantizer knobs.
+ * hadamard_n: 0 (no rotation), 16 or 32.  Each n-element sub-block of a
+ *   32-block is replaced by fl32(1/sqrt(n)) * H_n * (D x), H_n the Sylvester
+ *   Hadamard matrix in natural order, computed in fp32 by butterfly stages of
+ *   stride 1, 2, 4, ... (the stage order fixes the fp32 rounding).
+ * sign_mask: D = diag(d_i), d_i = -1 where bit (i mod n) is set; 0 gives the
+ *   deterministic Hadamard rotation, a random mask the randomized one (RHT).
+ *   The same mask must be used for both operands of one GEMM.
+ * sr_seed, sr_stream, sr_bits: the stochastic-rounding stream.  Element j of
+ *   the block with index b (its position in the scale array, row-major) takes
+ *   Philox4x32-10 with key (lo32(seed), hi32(seed)):
+ *     B = 16: counter (j>>3, lo32(b), hi32(b), stream), 16-bit half (j&1) of
+ *             output word ((j>>1)&3);
+ *     B = 8:  counter (j>>4, lo32(b), hi32(b), stream), byte (j&3) of word
+ *             ((j>>2)&3). */
+typedef struct {
+    int32_t grid;
+    int32_t round;
+    int32_t hadamard_n;
+    uint32_t sign_mask;
+    uint64_t sr_seed;
+    uint32_t sr_stream;
+    uint32_t sr_bits;
+} mxq_qconfig;
+
+/* A block-quantized tensor of `lines` lines, each `k` elements long (k % 32
+ * == 0), stored densely: codes [lines][k/32][16 or 24 bytes], scales
+ * [lines][k/32] E8M0 bytes (value 2^(s-127); 0xFF marks a non-finite block).
+ * codes must be 4-byte aligned. */
+typedef struct {
+    void *codes;
+    uint8_t *scales;
+    int32_t fmt;   /* MXQ_FMT_* */
+    int32_t grid;  /* MXQ_GRID_* of the stored values */
+} mxq_qtensor;
+
+/* Shrinkage-bias / SQNR sums over the rotated values y of the blocks with a
+ * finite scale (fp64, fixed-order reduction, so repeatable).  e is the
+ * block's scale exponent, a = |y| 2^-e, yhat the reconstruction. */
+typedef struct {
+    double sum_abs_y;          /* sum |y|                                     */
+    double sum_signed_err;     /* sum sign(y) (yhat - y)                      */
+    double sum_y2;             /* sum y^2                                     */
+    double sum_err2;           /* sum (yhat - y)^2                            */
+    double sum_err_norm;       /* sum (|yhat| - |y|) 2^-e                     */
+    double sum_err_norm_sat;   /* the same over elements with a > top level   */
+    double level_err_norm[8];  /* per magnitude code m: sum (G_m - a)         */
+    uint64_t n;                /* elements counted                            */
+    uint64_t n_saturated;      /* elements with a > top level                 */
+    uint64_t n_nonfinite_blocks;
+    uint64_t level_count[8];
+} mxq_stats;
+
+/* Fused rotate + scale + round + pack of a bf16 matrix x [rows x cols]
+ * (row-major, leading dimension ld_x elements, ld_x % 8 == 0, x 16-byte
+ * aligned), the quantization of every GEMM operand in the three training
+ * GEMMs (htx.com news, "Experimento de diagnostico"; the fused form follows
+ * the "Eficiencia" section of the shrinkage-bias summary).
+ *   row_out (may be NULL): blocks along cols, lines = rows, k = cols
+ *                          (needs cols % 32 == 0).
+ *   col_out (may be NULL): blocks along rows, written transposed: lines =
+ *                          cols, k = rows (needs rows % 32 == 0).
+ * At least one output is required; with both, one pass produces both (the
+ * row output rotates along cols, the column output along rows, each with the
+ * same mask).  Each output's grid must equal cfg->grid.
+ * Errors: NULL cfg/x/outputs -> MXQ_ERR_NULL; bad sizes -> MXQ_ERR_SHAPE;
+ * misaligned x/ld_x/codes -> MXQ_ERR_ALIGN; bad knobs -> MXQ_ERR_UNSUPPORTED. */
+mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
+                        int64_t ld_x, const mxq_qtensor *row_out, const mxq_qtensor *col_out,
+                        void *stream);
+
+/* Reconstruct yhat = (-1)^s G_m 2^(scale-127) (NaN for scale 0xFF) of a
+ * block-quantized tensor into out [lines x k] (leading dimension ld_out
+ * elements), as fp32 or bf16 (both exact).  The shared-exponent
+ * reconstruction of the htx.com news, section "Que es MXFP4?". */
+mxq_status mxq_dequantize(const mxq_qtensor *q, int64_t lines, int64_t k, int32_t out_dtype,
+                          void *out, int64_t ld_out, void *stream);
+
+/* The weight-gradient GEMM dW = dY^T X of the htx.com news ("Experimento de
+ * diagnostico"), on block-quantized operands that both run along the token
+ * axis: C [m x n] fp32 (leading dimension ldc) = A [m x k] * B [n x k]^T,
+ * where A = dY quantized column-wise (m = its column count) and B = X
+ * quantized column-wise.  Each product term carries both block scales; the
+ * sum is accumulated in fp32 on the block-scaled matrix cores.
+ * Operands: FP4 codes of the E2M1 grid, or E2M3 codes of either grid (A and
+ * B may differ).  k % 128 == 0; m, n >= 0 (any).  C is fully overwritten.
+ * Deterministic: no split-K, fixed summation order. */
+mxq_status mxq_wgrad_gemm(const mxq_qtensor *a, const mxq_qtensor *b, int64_t m, int64_t n,
+                          int64_t k, float *c, int64_t ldc, void *stream);
+
+/* Bias / SQNR statistics of the shrinkage-bias summary ("Metodologia 1",
+ * "Resultados Experimentais") for a tensor q produced by mxq_quantize from x
+ * with the same cfg and axis; the rotated y is recomputed exactly as the
+ * quantizer does.  `out` is a DEVICE pointer to one mxq_stats, fully
+ * overwritten.  `workspace` is a device buffer of at least
+ * mxq_bias_stats_workspace_size(rows, cols, axis) bytes. */
+mxq_status mxq_bias_stats(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
+                          int64_t ld_x, int32_t axis, const mxq_qtensor *q, mxq_stats *out,
+                          void *workspace, size_t ws_bytes, void *stream);
+size_t mxq_bias_stats_workspace_size(int64_t rows, int64_t cols, int32_t axis);
+
+/* The rounding step of mxq_quantize on its own, for checks of every input
+ * value: codes[i] = the sign-magnitude nibble of a[i] (a value already
+ * divided by its block scale 2^e, so |a| < 2^(emax+1) is the meaningful
+ * range; larger magnitudes saturate) under the grid and rounding of the
+ * shrinkage-bias summary ("Metodologia 1" RTNE, "Metodologia 2" SR).  For SR,
+ * rand[i] holds element i's sr_bits random bits (the caller draws them);
+ * rand may be NULL for RTNE.  a, rand, codes are device arrays of n items. */
+mxq_status mxq_round_to_grid(int32_t grid, int32_t round, int32_t sr_bits, const float *a,
+                             const uint16_t *rand, int64_t n, uint8_t *codes, void *stream);
+
+const char *mxq_status_string(mxq_status s);
+int32_t mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXQ_H */

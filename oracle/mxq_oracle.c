@@ -319,10 +319,11 @@ static int load_nibbles(const uint8_t *src, int fmt, int grid, uint8_t nib[32])
     return 0;
 }
 
-int orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
-                 const orc_qparams *p, int fmt, uint8_t *codes, uint8_t *scales)
+int orc_quantize_lines(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                       const orc_qparams *p, int fmt, int64_t line0, uint8_t *codes,
+                       uint8_t *scales)
 {
-    if (check_shape(rows, cols, ld, axis))
+    if (check_shape(rows, cols, ld, axis) || line0 < 0)
         return -1;
     int64_t lines = axis == ORC_AXIS_ROW ? rows : cols;
     int64_t k = axis == ORC_AXIS_ROW ? cols : rows;
@@ -332,13 +333,20 @@ int orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int 
         for (int64_t jb = 0; jb < nblk; ++jb) {
             float xb[32];
             uint8_t nib[32];
-            uint64_t b = (uint64_t)(line * nblk + jb);
+            int64_t local = line * nblk + jb;
+            uint64_t b = (uint64_t)((line0 + line) * nblk + jb);
             gather_block(x, ld, axis, line, jb, xb);
-            orc_quantize_block(xb, p, b, nib, &scales[b]);
-            store_codes(codes + (int64_t)b * bbytes, fmt, p->grid, nib);
+            orc_quantize_block(xb, p, b, nib, &scales[local]);
+            store_codes(codes + local * bbytes, fmt, p->grid, nib);
         }
     }
     return 0;
+}
+
+int orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                 const orc_qparams *p, int fmt, uint8_t *codes, uint8_t *scales)
+{
+    return orc_quantize_lines(x, rows, cols, ld, axis, p, fmt, 0, codes, scales);
 }
 
 int orc_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t lines, int64_t k,

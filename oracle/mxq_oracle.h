@@ -104,6 +104,13 @@ int orc_e2m3_code(int grid, int nibble);
 int orc_quantize(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
                  const orc_qparams *p, int fmt, uint8_t *codes, uint8_t *scales);
 
+/* The same for a slice: x holds only the lines line0 .. line0 + lines - 1 of a
+ * larger tensor (the rows for axis ROW, the columns for axis COL); block
+ * indices (which key the SR stream) are those of the whole tensor. */
+int orc_quantize_lines(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
+                       const orc_qparams *p, int fmt, int64_t line0, uint8_t *codes,
+                       uint8_t *scales);
+
 /* Dequantize [lines x k] blocks (k along the block axis) to fp64. */
 int orc_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t lines, int64_t k,
                    int grid, int fmt, double *out);

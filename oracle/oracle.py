@@ -81,6 +81,8 @@ def lib():
         L.orc_quantize_block.argtypes = [P, C.POINTER(QParams), C.c_uint64, P, P]
         L.orc_e2m3_code.argtypes = [C.c_int, C.c_int]
         L.orc_quantize.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int, P, P]
+        L.orc_quantize_lines.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int,
+                                         i64, P, P]
         L.orc_dequantize.argtypes = [P, P, i64, i64, C.c_int, C.c_int, P]
         L.orc_gemm_abt_f64.argtypes = [P, P, i64, i64, i64, P]
         L.orc_stats.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int, P, P,
@@ -191,6 +193,24 @@ def quantize(x, axis: int, p: QParams, fmt: int = FMT_FP4, ld: int | None = None
                             _ptr(scales))
     if rc != 0:
         raise ValueError(f"oracle quantize rejected shape {xb.shape} axis {axis}")
+    return codes, scales
+
+
+def quantize_lines(x, axis: int, p: QParams, line0: int, nlines: int, fmt: int = FMT_FP4):
+    """Quantize lines [line0, line0 + nlines) of the bf16 tensor x only (rows for
+    AXIS_ROW, columns for AXIS_COL), with the block indices of the whole tensor."""
+    xb = _bf16_bits(x)
+    sub = xb[line0:line0 + nlines] if axis == AXIS_ROW else xb[:, line0:line0 + nlines]
+    sub = np.ascontiguousarray(sub)
+    rows, cols = sub.shape
+    k = cols if axis == AXIS_ROW else rows
+    nblk = k // 32
+    codes = np.zeros((nlines, nblk * block_bytes(fmt)), dtype=np.uint8)
+    scales = np.zeros((nlines, nblk), dtype=np.uint8)
+    rc = lib().orc_quantize_lines(_ptr(sub), rows, cols, cols, axis, C.byref(p), fmt, line0,
+                                  _ptr(codes), _ptr(scales))
+    if rc != 0:
+        raise ValueError("oracle quantize_lines rejected shape")
     return codes, scales
 
 

@@ -1,0 +1,54 @@
+"""Shared helpers of the GPU parity tests (not a test module)."""
+import sys
+
+import numpy as np
+
+from fp4_microscaling_quantization_amd import synth
+
+
+def say(*args):
+    """Name the case about to run on the GPU (flushed, so a crash still shows it)."""
+    print("[gpu-case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+def dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a ROCm GPU"
+    return torch.device("cuda:0")
+
+
+def to_dev_bf16(xbits: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(xbits).view(np.int16)).to(dev()).view(torch.bfloat16)
+
+
+def host(t) -> np.ndarray:
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def special_matrix(rows: int, cols: int, seed: int) -> np.ndarray:
+    """bf16 bits with whole blocks (along both axes) of special values."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = g.standard_normal((rows, cols)).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(x)
+    flat = bits.reshape(-1)
+    n = flat.size
+    pick = lambda k: g.choice(n, size=min(k, n), replace=False)
+    flat[pick(n // 50)] = 0x0000                      # +0
+    flat[pick(n // 50)] = 0x8000                      # -0
+    flat[pick(n // 100)] = g.integers(1, 0x80, n // 100 if n >= 100 else 1, dtype=np.uint16)  # subnormal
+    flat[pick(max(n // 400, 1))] = 0x7F80             # +inf
+    flat[pick(max(n // 400, 1))] = 0xFF80             # -inf
+    flat[pick(max(n // 400, 1))] = 0x7FC1             # nan
+    flat[pick(n // 200)] = 0x7F7F                     # bf16 max (FWHT may overflow to inf)
+    # whole zero rows / columns / tiny rows
+    if rows > 3:
+        bits[1, :] = 0
+        bits[2, :] = (g.integers(1, 0x7F, cols) | (g.integers(0, 2, cols) << 15)).astype(np.uint16)
+    if cols > 5:
+        bits[:, 3] = 0x8000
+        bits[:, 5] = 0x0001
+    return bits

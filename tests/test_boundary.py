@@ -1,0 +1,134 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/mxq.h declares, and rejects bad arguments with the documented status
+before touching the GPU (no compute call is made here)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "mxq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for want in ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_bias_stats",
+                 "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_status_string",
+                 "mxq_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(mxq_lib):
+    L = mxq_lib.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert set(_declared_functions()) == set(mxq_lib.SYMBOLS)
+
+
+def test_abi_version_and_status_strings(mxq_lib):
+    L = mxq_lib.lib()
+    assert L.mxq_abi_version() == 1
+    for s in range(7):
+        assert mxq_lib.status_string(s)
+    assert mxq_lib.status_string(0) == "ok"
+
+
+def _fake(addr=0x10000):
+    return C.c_void_p(addr)
+
+
+def test_quantize_validation(mxq_lib):
+    L = mxq_lib.lib()
+    M = mxq_lib
+    good = M.qconfig()
+    out = M.QTensor(0x20000, 0x30000, M.FMT_FP4, M.GRID_E2M1)
+
+    def q(cfg, x=_fake(), rows=64, cols=64, ld=64, row=out, col=None):
+        return L.mxq_quantize(C.byref(cfg) if cfg is not None else None, x, rows, cols, ld,
+                              C.byref(row) if row is not None else None,
+                              C.byref(col) if col is not None else None, None)
+
+    assert q(None) == M.ERR_NULL
+    assert q(good, x=None) == M.ERR_NULL
+    assert q(good, row=None, col=None) == M.ERR_NULL
+    assert q(M.qconfig(grid=2)) == M.ERR_UNSUPPORTED
+    assert q(M.qconfig(round=5)) == M.ERR_UNSUPPORTED
+    assert q(M.qconfig(hadamard_n=8)) == M.ERR_UNSUPPORTED
+    assert q(M.qconfig(round=M.SR, sr_bits=12)) == M.ERR_UNSUPPORTED
+    assert q(good, cols=48, ld=48) == M.ERR_SHAPE                 # row blocks need cols % 32
+    assert q(good, rows=48, row=None, col=out) == M.ERR_SHAPE     # col blocks need rows % 32
+    assert q(good, rows=-1) == M.ERR_SHAPE
+    assert q(good, ld=32) == M.ERR_SHAPE                          # ld < cols
+    assert q(good, x=_fake(0x10002)) == M.ERR_ALIGN               # x not 16-byte aligned
+    assert q(good, ld=68) == M.ERR_ALIGN                          # ld % 8
+    bad_codes = M.QTensor(0x20002, 0x30000, M.FMT_FP4, M.GRID_E2M1)
+    assert q(good, row=bad_codes) == M.ERR_ALIGN
+    wrong_grid = M.QTensor(0x20000, 0x30000, M.FMT_FP4, M.GRID_E1M2)
+    assert q(good, row=wrong_grid) == M.ERR_UNSUPPORTED
+    bad_fmt = M.QTensor(0x20000, 0x30000, 7, M.GRID_E2M1)
+    assert q(good, row=bad_fmt) == M.ERR_UNSUPPORTED
+    null_codes = M.QTensor(None, 0x30000, M.FMT_FP4, M.GRID_E2M1)
+    assert q(good, row=null_codes) == M.ERR_NULL
+    # empty inputs are valid and launch nothing
+    assert q(good, rows=0) == M.OK
+    assert q(good, cols=0, ld=0) == M.OK
+
+
+def test_gemm_validation(mxq_lib):
+    L = mxq_lib.lib()
+    M = mxq_lib
+    a = M.QTensor(0x20000, 0x30000, M.FMT_FP4, M.GRID_E2M1)
+    b6 = M.QTensor(0x40000, 0x50000, M.FMT_E2M3, M.GRID_E1M2)
+    c = _fake(0x60000)
+
+    def g(a_, b_, m=64, n=64, k=256, cptr=c, ldc=64):
+        return L.mxq_wgrad_gemm(C.byref(a_) if a_ else None, C.byref(b_) if b_ else None, m, n, k,
+                                cptr, ldc, None)
+
+    assert g(None, a) == M.ERR_NULL
+    assert g(a, a, cptr=None) == M.ERR_NULL
+    e1m2_nibbles = M.QTensor(0x20000, 0x30000, M.FMT_FP4, M.GRID_E1M2)
+    assert g(e1m2_nibbles, a) == M.ERR_UNSUPPORTED     # no matrix-core type for E1M2 nibbles
+    assert g(a, b6, k=96) == M.ERR_SHAPE
+    assert g(a, b6, ldc=32) == M.ERR_SHAPE
+    assert g(a, b6, m=-3) == M.ERR_SHAPE
+    assert g(M.QTensor(0x20008, 0x30000, M.FMT_FP4, M.GRID_E2M1), b6) == M.ERR_ALIGN
+    assert g(a, b6, m=0) == M.OK
+
+
+def test_dequant_stats_round_validation(mxq_lib):
+    L = mxq_lib.lib()
+    M = mxq_lib
+    q = M.QTensor(0x20000, 0x30000, M.FMT_FP4, M.GRID_E2M1)
+    assert L.mxq_dequantize(None, 4, 64, 0, _fake(), 64, None) == M.ERR_NULL
+    assert L.mxq_dequantize(C.byref(q), 4, 48, 0, _fake(), 64, None) == M.ERR_SHAPE
+    assert L.mxq_dequantize(C.byref(q), 4, 64, 9, _fake(), 64, None) == M.ERR_UNSUPPORTED
+    assert L.mxq_dequantize(C.byref(q), 4, 64, 0, _fake(0x10004), 64, None) == M.ERR_ALIGN
+    cfg = M.qconfig()
+    ws = L.mxq_bias_stats_workspace_size(64, 64, 0)
+    assert ws > 0
+    assert L.mxq_bias_stats(C.byref(cfg), _fake(), 64, 64, 64, 0, C.byref(q), _fake(0x70000),
+                            None, 0, None) == M.ERR_WORKSPACE
+    assert L.mxq_bias_stats(C.byref(cfg), _fake(), 64, 64, 64, 0, C.byref(q), _fake(0x70000),
+                            _fake(0x80000), ws - 8, None) == M.ERR_WORKSPACE
+    assert L.mxq_bias_stats(C.byref(cfg), _fake(), 64, 64, 64, 3, C.byref(q), _fake(0x70000),
+                            _fake(0x80000), ws, None) == M.ERR_UNSUPPORTED
+    assert L.mxq_round_to_grid(3, 0, 16, _fake(), None, 10, _fake(), None) == M.ERR_UNSUPPORTED
+    assert L.mxq_round_to_grid(0, 1, 16, _fake(), None, 10, _fake(), None) == M.ERR_NULL
+    assert L.mxq_round_to_grid(0, 0, 16, _fake(), None, -1, _fake(), None) == M.ERR_SHAPE
+
+
+def test_product_path_has_no_oracle_dependency():
+    # the binding and the sources never reference the oracle
+    pkg = os.path.join(ROOT, "fp4_microscaling_quantization_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower() or f == "synth.py", f

@@ -1,0 +1,143 @@
+"""GPU parity of mxq_quantize against the CPU oracle: codes and scales must be
+bit-exact (integer / byte work), for every knob combination, ragged shapes,
+special values, padded leading dimensions, repeated runs, and -- at the full
+workload sizes, in the launch configuration the benchmark times -- on
+sampled lines checked one by one."""
+import numpy as np
+import pytest
+
+from fp4_microscaling_quantization_amd import synth
+from gpuhelp import dev, host, say, special_matrix, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+KNOBS = [(g, r, n) for g in (0, 1) for r in (0, 1) for n in (0, 16, 32)]
+
+
+def _knob_id(k):
+    g, r, n = k
+    return f"{'e2m1' if g == 0 else 'e1m2'}-{'rtne' if r == 0 else 'sr'}-h{n}"
+
+
+def _params(orc, grid, rnd, n, seed=0, sr_bits=16):
+    mask = synth.sign_mask(100 + seed, n) if n else 0
+    return dict(grid=grid, round=rnd, hadamard_n=n, sign_mask=mask, sr_seed=0x5EED0000 + seed,
+                sr_stream=seed, sr_bits=sr_bits)
+
+
+def _check(orc, x, knobs, row_fmt=None, col_fmt=None, ld=None, tag=""):
+    from fp4_microscaling_quantization_amd import mxq
+    rows, cols = x.shape
+    say(tag, x.shape, knobs, row_fmt, col_fmt, ld)
+    if ld is None:
+        xt = to_dev_bf16(x)
+    else:
+        import torch
+        wide = np.zeros((rows, ld), np.uint16)
+        wide[:, :cols] = x
+        xt = to_dev_bf16(wide)[:, :cols]
+    q = mxq.quantize(xt, row=row_fmt is not None, col=col_fmt is not None,
+                     row_fmt=row_fmt or 0, col_fmt=col_fmt or 0, **knobs)
+    p = orc.qparams(**knobs)
+    if row_fmt is not None:
+        c, s = orc.quantize(x, orc.AXIS_ROW, p, row_fmt)
+        gc, gs = host(q["row"][0]), host(q["row"][1])
+        assert np.array_equal(gs, s), "row scales differ"
+        assert np.array_equal(gc, c), f"row codes differ at {np.argwhere(gc != c)[:5]}"
+    if col_fmt is not None:
+        c, s = orc.quantize(x, orc.AXIS_COL, p, col_fmt)
+        gc, gs = host(q["col"][0]), host(q["col"][1])
+        assert np.array_equal(gs, s), "col scales differ"
+        assert np.array_equal(gc, c), f"col codes differ at {np.argwhere(gc != c)[:5]}"
+
+
+@pytest.mark.parametrize("shape", [(77, 96), (33, 4128), (1, 32), (256, 512)])
+@pytest.mark.parametrize("knobs", KNOBS, ids=_knob_id)
+def test_row_parity(orc, shape, knobs):
+    x = synth.normal_outlier_channels(*shape, seed=shape[0], ch_seed=shape[1], frac=0.05)
+    for fmt in (0, 1):
+        _check(orc, x, _params(orc, *knobs, seed=shape[0]), row_fmt=fmt, tag="row")
+
+
+@pytest.mark.parametrize("shape", [(96, 100), (64, 130), (256, 256), (32, 8), (160, 1)])
+@pytest.mark.parametrize("knobs", KNOBS, ids=_knob_id)
+def test_col_parity(orc, shape, knobs):
+    x = synth.laplace_outlier_entries(*shape, seed=shape[1], out_seed=3, frac=0.01)
+    for fmt in (0, 1):
+        _check(orc, x, _params(orc, *knobs, seed=shape[1]), col_fmt=fmt, tag="col")
+
+
+@pytest.mark.parametrize("shape", [(160, 288), (32, 32), (128, 4096), (288, 96)])
+@pytest.mark.parametrize("knobs", KNOBS, ids=_knob_id)
+def test_dual_parity(orc, shape, knobs):
+    x = synth.normal(*shape, seed=7, std=0.02)
+    _check(orc, x, _params(orc, *knobs, seed=5), row_fmt=0, col_fmt=1, tag="dual")
+    _check(orc, x, _params(orc, *knobs, seed=6), row_fmt=1, col_fmt=0, tag="dual")
+
+
+@pytest.mark.parametrize("knobs", KNOBS, ids=_knob_id)
+def test_special_values(orc, knobs):
+    x = special_matrix(96, 160, seed=11)
+    p = _params(orc, *knobs, seed=9)
+    _check(orc, x, p, row_fmt=0, tag="special-row")
+    _check(orc, x, p, col_fmt=1, tag="special-col")
+    _check(orc, x, p, row_fmt=1, col_fmt=0, tag="special-dual")
+
+
+@pytest.mark.parametrize("knobs", [(0, 0, 16), (1, 1, 32), (1, 0, 0)], ids=_knob_id)
+def test_padded_leading_dimension(orc, knobs):
+    x = synth.normal(64, 96, seed=3)
+    p = _params(orc, *knobs, seed=2)
+    _check(orc, x, p, row_fmt=0, ld=104, tag="ld-row")
+    _check(orc, x, p, col_fmt=0, ld=136, tag="ld-col")
+    _check(orc, x, p, row_fmt=0, col_fmt=1, ld=128, tag="ld-dual")
+
+
+def test_sr_8_bit_stream(orc):
+    x = synth.normal(64, 256, seed=4)
+    for grid in (0, 1):
+        p = _params(orc, grid, 1, 16, seed=8, sr_bits=8)
+        _check(orc, x, p, row_fmt=0, tag="sr8-row")
+        _check(orc, x, p, col_fmt=0, tag="sr8-col")
+
+
+def test_repeatable_bitwise(orc):
+    from fp4_microscaling_quantization_amd import mxq
+    x = synth.laplace_outlier_entries(512, 384, seed=1, out_seed=2)
+    xt = to_dev_bf16(x)
+    knobs = _params(orc, 1, 1, 16, seed=3)
+    say("repeat", x.shape)
+    a = mxq.quantize(xt, row=True, col=True, row_fmt=0, col_fmt=1, **knobs)
+    b = mxq.quantize(xt, row=True, col=True, row_fmt=0, col_fmt=1, **knobs)
+    for key in ("row", "col"):
+        for i in (0, 1):
+            assert np.array_equal(host(a[key][i]), host(b[key][i]))
+
+
+def _sample_lines(lines: int):
+    g = np.random.Generator(np.random.PCG64(lines))
+    mid = sorted(g.choice(np.arange(8, lines - 8), size=3, replace=False).tolist())
+    return [0] + mid + [lines - 8]
+
+
+@pytest.mark.parametrize("case", synth.workload_cases(), ids=lambda c: c.name)
+def test_full_size_workloads_sampled(orc, case):
+    """Full-size tensors in the benchmark's launch configuration; the oracle
+    checks 8-line slices at the start, three random places and the end of
+    every output (line = row for row-wise, column for column-wise)."""
+    from fp4_microscaling_quantization_amd import mxq
+    x = case.make()
+    say("full", case.name, x.shape)
+    xt = to_dev_bf16(x)
+    q = mxq.quantize(xt, row=case.row_out, col=case.col_out, row_fmt=case.fmt, col_fmt=case.fmt,
+                     **case.knobs())
+    p = orc.qparams(**case.knobs())
+    for axis, key in ((orc.AXIS_ROW, "row"), (orc.AXIS_COL, "col")):
+        if key not in q:
+            continue
+        gc, gs = host(q[key][0]), host(q[key][1])
+        lines = gs.shape[0]
+        for l0 in _sample_lines(lines):
+            c, s = orc.quantize_lines(x, axis, p, l0, 8, case.fmt)
+            assert np.array_equal(gs[l0:l0 + 8], s), (key, l0)
+            assert np.array_equal(gc[l0:l0 + 8], c), (key, l0)

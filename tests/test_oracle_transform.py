@@ -160,3 +160,12 @@ def test_gemm_of_dequantized_integer_codes_is_exact(orc):
         c = orc.gemm_abt_f64(a, a)
         ref = (a.astype(np.float64) * 2 ** 4).astype(np.int64)
         assert np.array_equal(c * 2 ** 8, (ref @ ref.T).astype(np.float64))
+
+
+def test_quantize_lines_matches_whole_tensor(orc):
+    x = _rand_bf16(96, 64, 12)
+    p = orc.qparams(grid=1, round=1, hadamard_n=16, sign_mask=0xBEEF, sr_seed=99)
+    for axis in (orc.AXIS_ROW, orc.AXIS_COL):
+        c, s = orc.quantize(x, axis, p)
+        c2, s2 = orc.quantize_lines(x, axis, p, 17, 9)
+        assert np.array_equal(c[17:26], c2) and np.array_equal(s[17:26], s2)
