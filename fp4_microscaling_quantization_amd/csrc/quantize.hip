@@ -35,6 +35,17 @@ __device__ __forceinline__ void widen8(const uint4 &q, uint32_t sg, float (&v)[8
     }
 }
 
+// 8 consecutive bf16 through 2-byte loads (rows that are not 16-byte aligned).
+__device__ __forceinline__ uint4 load8_scalar(const uint16_t *__restrict__ p)
+{
+    uint32_t h[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        h[j] = p[j];
+    return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                      h[6] | (h[7] << 16));
+}
+
 // Store this lane's slice of block `blk`: FP4 4 bytes at 4*pos, or E2M3 in
 // pairs (the even lane writes 12 bytes for itself and its XP partner).  All
 // lanes of the block must call it (the E2M3 path exchanges by DPP).
@@ -63,7 +74,7 @@ __device__ __forceinline__ void store_slice(uint8_t *__restrict__ codes, uint8_t
 
 template <int GRID, int ROUND, int HN>
 __global__ __launch_bounds__(256) void k_quant_row(const uint16_t *__restrict__ x, uint64_t nblocks,
-                                                   uint32_t nbr, int64_t ld, int dense,
+                                                   uint32_t nbr, int64_t ld, int dense, int vec,
                                                    uint8_t *__restrict__ codes,
                                                    uint8_t *__restrict__ scales, int fmt, QKnobs kn)
 {
@@ -83,7 +94,7 @@ __global__ __launch_bounds__(256) void k_quant_row(const uint16_t *__restrict__ 
                 const uint64_t r = b / nbr;
                 off = (int64_t)r * ld + (int64_t)(b - r * nbr) * 32 + 8 * pos;
             }
-            raw[u] = *reinterpret_cast<const uint4 *>(x + off);
+            raw[u] = vec ? *reinterpret_cast<const uint4 *>(x + off) : load8_scalar(x + off);
         }
     }
 #pragma unroll
@@ -104,7 +115,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
                                                     uint8_t *__restrict__ rscales, int rfmt,
                                                     uint8_t *__restrict__ ccodes,
                                                     uint8_t *__restrict__ cscales, int cfmt,
-                                                    QKnobs kn)
+                                                    int vec, QKnobs kn)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int g = lane >> 4, l16 = lane & 15, qr = l16 & 3, qc = l16 >> 2;
@@ -115,7 +126,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
     const int64_t c0 = (int64_t)blockIdx.x * 128 + 32 * g + 8 * qc;
 
     uint4 raw[8];
-    if (c0 + 8 <= cols) {
+    if (vec && c0 + 8 <= cols) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             raw[i] = *reinterpret_cast<const uint4 *>(x + (r0 + i) * ld + c0);
@@ -201,6 +212,7 @@ struct QuantLaunch {
     int rfmt;
     uint8_t *ccodes, *cscales;
     int cfmt;
+    int vec;  // x 16-byte aligned and ld % 8 == 0: 128-bit loads
     QKnobs kn;
     hipStream_t s;
 };
@@ -214,18 +226,18 @@ hipError_t launch_quant(const QuantLaunch &q)
         const uint64_t nblocks = (uint64_t)q.rows * nbr;
         const uint64_t grid = (nblocks + 64 * kRowU - 1) / (64 * kRowU);
         hipLaunchKernelGGL((k_quant_row<GRID, ROUND, HN>), dim3((unsigned)grid), dim3(256), 0, q.s,
-                           q.x, nblocks, (uint32_t)nbr, q.ld, (int)(q.ld == q.cols), q.rcodes,
-                           q.rscales, q.rfmt, q.kn);
+                           q.x, nblocks, (uint32_t)nbr, q.ld, (int)(q.ld == q.cols), q.vec,
+                           q.rcodes, q.rscales, q.rfmt, q.kn);
     } else {
         const dim3 grid((unsigned)((q.cols + 127) / 128), (unsigned)((q.rows + 127) / 128));
         if (rows_out)
             hipLaunchKernelGGL((k_quant_tile<GRID, ROUND, HN, true, true>), grid, dim3(256), 0, q.s,
                                q.x, q.rows, q.cols, q.ld, q.rcodes, q.rscales, q.rfmt, q.ccodes,
-                               q.cscales, q.cfmt, q.kn);
+                               q.cscales, q.cfmt, q.vec, q.kn);
         else
             hipLaunchKernelGGL((k_quant_tile<GRID, ROUND, HN, false, true>), grid, dim3(256), 0,
                                q.s, q.x, q.rows, q.cols, q.ld, q.rcodes, q.rscales, q.rfmt,
-                               q.ccodes, q.cscales, q.cfmt, q.kn);
+                               q.ccodes, q.cscales, q.cfmt, q.vec, q.kn);
     }
     return hipGetLastError();
 }
@@ -304,7 +316,7 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
         return st;
     if (col_out && (st = check_qtensor_out(col_out, cfg->grid)))
         return st;
-    if (reinterpret_cast<uintptr_t>(x) % 16 || ld_x % 8)
+    if (reinterpret_cast<uintptr_t>(x) % 2)
         return MXQ_ERR_ALIGN;
     // grid-size limits of the launches (2^31 workgroups / 65535 row tiles)
     if (col_out && (rows + 127) / 128 > 65535)
@@ -323,6 +335,7 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
     q.ccodes = col_out ? static_cast<uint8_t *>(col_out->codes) : nullptr;
     q.cscales = col_out ? col_out->scales : nullptr;
     q.cfmt = col_out ? col_out->fmt : 0;
+    q.vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0 && ld_x % 8 == 0) ? 1 : 0;
     q.kn = make_knobs(cfg);
     q.s = static_cast<hipStream_t>(stream);
 

@@ -136,8 +136,9 @@ typedef struct {
 } mxq_stats;
 
 /* Fused rotate + scale + round + pack of a bf16 matrix x [rows x cols]
- * (row-major, leading dimension ld_x elements, ld_x % 8 == 0, x 16-byte
- * aligned), the quantization of every GEMM operand in the three training
+ * (row-major, leading dimension ld_x >= cols elements, x 2-byte aligned;
+ * 128-bit loads are used when x is 16-byte aligned and ld_x % 8 == 0, else
+ * 16-bit loads), the quantization of every GEMM operand in the three training
  * GEMMs (htx.com news, "Experimento de diagnostico"; the fused form follows
  * the "Eficiencia" section of the shrinkage-bias summary).
  *   row_out (may be NULL): blocks along cols, lines = rows, k = cols
@@ -148,7 +149,7 @@ typedef struct {
  * row output rotates along cols, the column output along rows, each with the
  * same mask).  Each output's grid must equal cfg->grid.
  * Errors: NULL cfg/x/outputs -> MXQ_ERR_NULL; bad sizes -> MXQ_ERR_SHAPE;
- * misaligned x/ld_x/codes -> MXQ_ERR_ALIGN; bad knobs -> MXQ_ERR_UNSUPPORTED. */
+ * misaligned x/codes -> MXQ_ERR_ALIGN; bad knobs -> MXQ_ERR_UNSUPPORTED. */
 mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
                         int64_t ld_x, const mxq_qtensor *row_out, const mxq_qtensor *col_out,
                         void *stream);
