@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X.
+
+One step = the weight-gradient step of a Llama-3.1-8B-shaped linear layer at
+T = 8192 tokens, the whole hot path:
+  1. fused H16 RHT + MX block-32 quantize of dY [8192 x 4096] along T
+     (column-wise, uniform E1M2 grid, Philox stochastic rounding, FP6 E2M3
+     operand form),
+  2. the same for X [8192 x 4096] (E1M2, RTNE),
+  3. the block-scaled GEMM dW [4096 x 4096] = dY^T X on the FP6 matrix cores.
+Inputs are synthetic (seeded numpy), resident in HBM before timing.  Four
+input/output sets rotate so consecutive steps do not hit in the 256 MB
+last-level cache.
+
+The JSON line reports the fused quantize bandwidth as `value` (algorithmic
+bytes of the two quantize launches / their event-timed duration), the GEMM
+rate under `gemm`, the roofline of the dominant kernel and of each kernel,
+and the CPU oracle timed on a bounded sample as `cpu_baseline`.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"fp4": 10100.0, "fp6": 10100.0}   # dense, TFLOP/s
+
+T, N, K = 8192, 4096, 4096     # tokens, out features (dY cols), in features (X cols)
+
+
+def quant_bytes_per_elem(fmt: int) -> float:
+    # read bf16 (2 B) + write codes (0.5 B FP4 / 0.75 B E2M3) + 1 scale byte per 32
+    return 2.0 + (0.5 if fmt == 0 else 0.75) + 1.0 / 32
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=4, help="rotating input/output sets")
+    ap.add_argument("--variant", choices=["e1m2", "e2m1"], default="e1m2",
+                    help="e1m2: UFP4 operands as FP6 E2M3; e2m1: MXFP4 operands as FP4")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from fp4_microscaling_quantization_amd import mxq, synth
+
+    mxq.lib()  # fail loudly if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    grid = mxq.GRID_E1M2 if args.variant == "e1m2" else mxq.GRID_E2M1
+    fmt = mxq.FMT_E2M3 if args.variant == "e1m2" else mxq.FMT_FP4
+    signs = synth.sign_mask(synth.SIGNS_WGRAD, 16)
+    cfg_dy = mxq.qconfig(grid=grid, round=mxq.SR, hadamard_n=16, sign_mask=signs,
+                         sr_seed=synth.SR_SEED_WGRAD)
+    cfg_x = mxq.qconfig(grid=grid, round=mxq.RTNE, hadamard_n=16, sign_mask=signs)
+
+    t0 = time.time()
+    dy_np = synth.dy_8192x4096()
+    x_np = synth.x_wgrad_8192x4096()
+    print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    sets = []
+    dy0, x0 = to_dev(dy_np), to_dev(x_np)
+    for s in range(args.sets):
+        dy = dy0 if s == 0 else dy0.clone()
+        xx = x0 if s == 0 else x0.clone()
+        qd = mxq.empty_qtensor(N, T, fmt, dev)
+        qx = mxq.empty_qtensor(K, T, fmt, dev)
+        c = torch.empty((N, K), dtype=torch.float32, device=dev)
+        sets.append((dy, xx, qd, qx, c))
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        dy, xx, qd, qx, c = sets[i % len(sets)]
+        if ev is not None:
+            ev[0].record()
+        mxq.quantize_into(cfg_dy, dy, col=(qd[0], qd[1], fmt))
+        if ev is not None:
+            ev[1].record()
+        mxq.quantize_into(cfg_x, xx, col=(qx[0], qx[1], fmt))
+        if ev is not None:
+            ev[2].record()
+        mxq.wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, out=c)
+        if ev is not None:
+            ev[3].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+
+    q_dy = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3     # seconds
+    q_x = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    gm = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
+    elems = T * N
+    qbytes = elems * quant_bytes_per_elem(fmt)                           # per launch
+    flops = 2.0 * N * K * T
+    q_gbs = 2 * qbytes * args.steps / (q_dy.sum() + q_x.sum()) / 1e9
+    g_tflops = flops * args.steps / gm.sum() / 1e12
+    mfma_peak = MFMA_PEAK_TFLOPS["fp6" if fmt == mxq.FMT_E2M3 else "fp4"]
+
+    kernels = {
+        "quantize_dy_col_sr": {"bound": "hbm", "avg_us": q_dy.mean() * 1e6,
+                               "achieved": qbytes / q_dy.mean() / 1e9, "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s"},
+        "quantize_x_col_rtne": {"bound": "hbm", "avg_us": q_x.mean() * 1e6,
+                                "achieved": qbytes / q_x.mean() / 1e9, "peak": HBM_PEAK_GBS,
+                                "unit": "GB/s"},
+        "wgrad_gemm": {"bound": "mfma", "avg_us": gm.mean() * 1e6,
+                       "achieved": flops / gm.mean() / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
+    }
+    for k_ in kernels.values():
+        k_["frac"] = k_["achieved"] / k_["peak"]
+        for f in ("avg_us", "achieved", "frac"):
+            k_[f] = round(k_[f], 4)
+    dom_name = max(kernels, key=lambda n: kernels[n]["avg_us"])
+    dom = dict(kernels[dom_name])
+    dom["kernel"] = dom_name
+    dom["traffic"] = None
+    dom.pop("avg_us")
+
+    rec = {
+        "metric": "fused RHT+MXFP4 quantize GB/s (% HBM peak); MXFP4 Wgrad GEMM TFLOPS",
+        "value": round(q_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"wgrad step T={T}: dY[{T}x{N}] and X[{T}x{K}] bf16 -> H16 RHT + "
+                        f"column-wise MX block-32 {args.variant.upper()} "
+                        f"({'FP6 E2M3' if fmt == mxq.FMT_E2M3 else 'FP4'} operands; dY SR, X RTNE)"
+                        f" -> dW[{N}x{K}] fp32 block-scaled GEMM",
+            "global_batch": T,
+            "seq_len": T,
+            "parallelism": "none (1 GPU)",
+            "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+        },
+        "gemm": {"value": round(g_tflops, 2), "unit": "TFLOP/s", "peak": mfma_peak,
+                 "frac": round(g_tflops / mfma_peak, 4)},
+        "roofline": dom,
+        "kernels": kernels,
+    }
+
+    if args.copy_calib:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        rec["copy_calib_bytes"] = 1 << 30
+
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, args.cpu_seconds)
+
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the same step:
+    column-wise quantization of the first c columns of dY and of X (all 8192
+    tokens each), then the fp64 product of 32 x 32 of the resulting outputs."""
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    pd = orc.qparams(grid=cfg_dy.grid, round=cfg_dy.round, hadamard_n=cfg_dy.hadamard_n,
+                     sign_mask=cfg_dy.sign_mask, sr_seed=cfg_dy.sr_seed)
+    px = orc.qparams(grid=cfg_x.grid, round=cfg_x.round, hadamard_n=cfg_x.hadamard_n,
+                     sign_mask=cfg_x.sign_mask)
+    # calibrate on 8 columns, then size the sample to the budget
+    t0 = time.perf_counter()
+    orc.quantize_lines(dy_np, orc.AXIS_COL, pd, 0, 8, fmt)
+    orc.quantize_lines(x_np, orc.AXIS_COL, px, 0, 8, fmt)
+    per_col = (time.perf_counter() - t0) / 8
+    ncol = int(max(8, min(N, budget_s / max(per_col, 1e-9))))
+    t0 = time.perf_counter()
+    cd, sd = orc.quantize_lines(dy_np, orc.AXIS_COL, pd, 0, ncol, fmt)
+    cx, sx = orc.quantize_lines(x_np, orc.AXIS_COL, px, 0, ncol, fmt)
+    tq = time.perf_counter() - t0
+    qbytes = 2 * ncol * T * quant_bytes_per_elem(fmt)
+    a = orc.dequantize(cd[:32], sd[:32], grid, fmt)
+    b = orc.dequantize(cx[:32], sx[:32], grid, fmt)
+    t1 = time.perf_counter()
+    orc.gemm_abt_f64(a, b)
+    tg = time.perf_counter() - t1
+    return {
+        "value": round(qbytes / tq / 1e9, 5),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"column-wise quantize of {ncol} of {N} columns of dY and of X (T={T}) "
+                  f"in {tq:.1f}s; fp64 GEMM of 32x32 outputs over K={T} in {tg:.3f}s",
+        "gemm_tflops": round(2.0 * 32 * 32 * T / tg / 1e12, 6),
+        "cpu": _cpu_model(),
+    }
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()
