@@ -90,8 +90,8 @@ def main():
     for s in range(args.sets):
         dy = dy0 if s == 0 else dy0.clone()
         xx = x0 if s == 0 else x0.clone()
-        qd = mxq.empty_qtensor(N, T, fmt, dev)
-        qx = mxq.empty_qtensor(K, T, fmt, dev)
+        qd = mxq.empty_qtensor(N, T, fmt, dev, mxq.LAYOUT_MFMA)
+        qx = mxq.empty_qtensor(K, T, fmt, dev, mxq.LAYOUT_MFMA)
         c = torch.empty((N, K), dtype=torch.float32, device=dev)
         sets.append((dy, xx, qd, qx, c))
     torch.cuda.synchronize()
@@ -100,13 +100,14 @@ def main():
         dy, xx, qd, qx, c = sets[i % len(sets)]
         if ev is not None:
             ev[0].record()
-        mxq.quantize_into(cfg_dy, dy, col=(qd[0], qd[1], fmt))
+        mxq.quantize_into(cfg_dy, dy, col=(qd[0], qd[1], fmt, mxq.LAYOUT_MFMA))
         if ev is not None:
             ev[1].record()
-        mxq.quantize_into(cfg_x, xx, col=(qx[0], qx[1], fmt))
+        mxq.quantize_into(cfg_x, xx, col=(qx[0], qx[1], fmt, mxq.LAYOUT_MFMA))
         if ev is not None:
             ev[2].record()
-        mxq.wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, out=c)
+        mxq.wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, out=c,
+                       layout=mxq.LAYOUT_MFMA, m=N, n=K, k=T)
         if ev is not None:
             ev[3].record()
 
@@ -168,7 +169,8 @@ def main():
         "config": {
             "workload": f"wgrad step T={T}: dY[{T}x{N}] and X[{T}x{K}] bf16 -> H16 RHT + "
                         f"column-wise MX block-32 {args.variant.upper()} "
-                        f"({'FP6 E2M3' if fmt == mxq.FMT_E2M3 else 'FP4'} operands; dY SR, X RTNE)"
+                        f"({'FP6 E2M3' if fmt == mxq.FMT_E2M3 else 'FP4'} operands in the matrix-core "
+                        f"layout; dY SR, X RTNE)"
                         f" -> dW[{N}x{K}] fp32 block-scaled GEMM",
             "global_batch": T,
             "seq_len": T,

@@ -59,10 +59,26 @@ __device__ __forceinline__ uint32_t load_nibbles8(const uint8_t *codes, int fmt,
     return w;
 }
 
+// Block (line, jb) -> its block index in the code array and its scale byte
+// offset, for both layouts (see MXQ_LAYOUT_MFMA in mxq.h).
+__device__ __forceinline__ void block_place(int layout, int64_t line, int64_t jb, int64_t nbk,
+                                            int64_t ntiles, uint64_t *cblk, uint64_t *soff)
+{
+    if (layout == MXQ_LAYOUT_ROWS) {
+        *cblk = (uint64_t)(line * nbk + jb);
+        *soff = *cblk;
+    } else {
+        const uint64_t lane = 16 * (uint64_t)(jb & 3) + (uint64_t)(line & 15);
+        *cblk = ((uint64_t)(jb >> 2) * ntiles + (uint64_t)(line >> 4)) * 64 + lane;
+        *soff = (((uint64_t)(jb >> 4) * ntiles + (uint64_t)(line >> 4)) * 64 + lane) * 4 +
+                (uint64_t)((jb >> 2) & 3);
+    }
+}
+
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ codes,
                                                  const uint8_t *__restrict__ scales, int fmt,
-                                                 int grid, int64_t lines, int64_t nbk, int out_bf16,
-                                                 void *__restrict__ out, int64_t ld_out)
+                                                 int grid, int layout, int64_t lines, int64_t nbk,
+                                                 int out_bf16, void *__restrict__ out, int64_t ld_out)
 {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t b = gid >> 2;
@@ -70,8 +86,10 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t *__restrict__ cod
     if (b >= lines * nbk)
         return;
     const int64_t line = b / nbk, jb = b - line * nbk;
-    const uint32_t sc = scales[b];
-    const uint32_t w = load_nibbles8(codes, fmt, grid, (uint64_t)b, pos);
+    uint64_t cblk, soff;
+    block_place(layout, line, jb, nbk, (lines + 15) / 16, &cblk, &soff);
+    const uint32_t sc = scales[soff];
+    const uint32_t w = load_nibbles8(codes, fmt, grid, cblk, pos);
     float v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -283,7 +301,11 @@ extern "C" mxq_status mxq_dequantize(const mxq_qtensor *q, int64_t lines, int64_
         return MXQ_ERR_UNSUPPORTED;
     if (out_dtype != MXQ_OUT_F32 && out_dtype != MXQ_OUT_BF16)
         return MXQ_ERR_UNSUPPORTED;
+    if (q->layout != MXQ_LAYOUT_ROWS && q->layout != MXQ_LAYOUT_MFMA)
+        return MXQ_ERR_UNSUPPORTED;
     if (lines < 0 || k < 0 || k % 32 || ld_out < k)
+        return MXQ_ERR_SHAPE;
+    if (q->layout == MXQ_LAYOUT_MFMA && k % 128)
         return MXQ_ERR_SHAPE;
     const int esz = out_dtype == MXQ_OUT_F32 ? 4 : 2;
     if (reinterpret_cast<uintptr_t>(out) % 16 || (ld_out * esz) % 16 ||
@@ -294,8 +316,8 @@ extern "C" mxq_status mxq_dequantize(const mxq_qtensor *q, int64_t lines, int64_
     const int64_t threads = lines * (k / 32) * 4;
     hipLaunchKernelGGL(k_dequant, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
                        static_cast<hipStream_t>(stream), static_cast<const uint8_t *>(q->codes),
-                       q->scales, q->fmt, q->grid, lines, k / 32, (int)(out_dtype == MXQ_OUT_BF16),
-                       out, ld_out);
+                       q->scales, q->fmt, q->grid, q->layout, lines, k / 32,
+                       (int)(out_dtype == MXQ_OUT_BF16), out, ld_out);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
 }
 
@@ -321,7 +343,7 @@ extern "C" mxq_status mxq_bias_stats(const mxq_qconfig *cfg, const void *x, int6
         return MXQ_ERR_UNSUPPORTED;
     if (q->fmt != MXQ_FMT_FP4 && q->fmt != MXQ_FMT_E2M3)
         return MXQ_ERR_UNSUPPORTED;
-    if (q->grid != cfg->grid)
+    if (q->grid != cfg->grid || q->layout != MXQ_LAYOUT_ROWS)
         return MXQ_ERR_UNSUPPORTED;
     if (rows < 0 || cols < 0 || ld_x < cols)
         return MXQ_ERR_SHAPE;

@@ -10,7 +10,7 @@
 namespace mxq {
 
 mxq_status check_qconfig(const mxq_qconfig *cfg);
-mxq_status check_qtensor_out(const mxq_qtensor *t, int32_t grid);
+mxq_status check_qtensor_out(const mxq_qtensor *t, int32_t grid, int64_t k);
 QKnobs make_knobs(const mxq_qconfig *cfg);
 
 }  // namespace mxq

@@ -46,37 +46,63 @@ __device__ __forceinline__ uint4 load8_scalar(const uint16_t *__restrict__ p)
                       h[6] | (h[7] << 16));
 }
 
-// Store this lane's slice of block `blk`: FP4 4 bytes at 4*pos, or E2M3 in
-// pairs (the even lane writes 12 bytes for itself and its XP partner).  All
-// lanes of the block must call it (the E2M3 path exchanges by DPP).
-template <int GRID, int XP>
-__device__ __forceinline__ void store_slice(uint8_t *__restrict__ codes, uint8_t *__restrict__ scales,
-                                            int fmt, uint64_t blk, int pos, uint32_t w, uint32_t sc,
-                                            bool valid)
+// Where an output's blocks go (MXQ_LAYOUT_ROWS or MXQ_LAYOUT_MFMA).
+struct OutDesc {
+    uint8_t *codes;
+    uint8_t *scales;
+    int fmt;
+    int layout;
+    uint64_t nbk;     // blocks per line
+    uint64_t ntiles;  // 16-line tiles (MFMA layout)
+};
+
+__device__ __forceinline__ uint64_t code_offset(const OutDesc &o, uint64_t line, uint64_t jb, int bb)
 {
-    if (fmt == MXQ_FMT_FP4) {
+    if (o.layout == MXQ_LAYOUT_ROWS)
+        return (line * o.nbk + jb) * bb;
+    // [step = jb / 4][tile = line / 16][lane = 16 (jb % 4) + line % 16]
+    return (((jb >> 2) * o.ntiles + (line >> 4)) * 64 + 16 * (jb & 3) + (line & 15)) * bb;
+}
+
+__device__ __forceinline__ uint64_t scale_offset(const OutDesc &o, uint64_t line, uint64_t jb)
+{
+    if (o.layout == MXQ_LAYOUT_ROWS)
+        return line * o.nbk + jb;
+    // [group = jb / 16][tile][lane] words, byte = step within the group
+    return (((jb >> 4) * o.ntiles + (line >> 4)) * 64 + 16 * (jb & 3) + (line & 15)) * 4 +
+           ((jb >> 2) & 3);
+}
+
+// Store this lane's slice of block (line, jb): FP4 4 bytes at 4*pos, or E2M3
+// in pairs (the even lane writes 12 bytes for itself and its XP partner).
+// All lanes of the block must call it (the E2M3 path exchanges by DPP).
+template <int GRID, int XP>
+__device__ __forceinline__ void store_slice(const OutDesc &o, uint64_t line, uint64_t jb, int pos,
+                                            uint32_t w, uint32_t sc, bool valid)
+{
+    if (o.fmt == MXQ_FMT_FP4) {
         if (valid)
-            *reinterpret_cast<uint32_t *>(codes + blk * 16 + 4 * pos) = w;
+            *reinterpret_cast<uint32_t *>(o.codes + code_offset(o, line, jb, 16) + 4 * pos) = w;
     } else {
         const uint64_t own = e2m3_pack8<GRID>(w);
         const uint32_t lo = (uint32_t)own, hi = (uint32_t)(own >> 32);
         const uint32_t plo = lane_xor<XP>(lo), phi = lane_xor<XP>(hi);
         if (valid && !(pos & 1)) {
-            uint32_t *d = reinterpret_cast<uint32_t *>(codes + blk * 24 + 12 * (pos >> 1));
+            uint32_t *d = reinterpret_cast<uint32_t *>(o.codes + code_offset(o, line, jb, 24) +
+                                                       12 * (pos >> 1));
             d[0] = lo;
             d[1] = hi | (plo << 16);
             d[2] = (plo >> 16) | (phi << 16);
         }
     }
     if (valid && pos == 0)
-        scales[blk] = (uint8_t)sc;
+        o.scales[scale_offset(o, line, jb)] = (uint8_t)sc;
 }
 
 template <int GRID, int ROUND, int HN>
 __global__ __launch_bounds__(256) void k_quant_row(const uint16_t *__restrict__ x, uint64_t nblocks,
                                                    uint32_t nbr, int64_t ld, int dense, int vec,
-                                                   uint8_t *__restrict__ codes,
-                                                   uint8_t *__restrict__ scales, int fmt, QKnobs kn)
+                                                   OutDesc out, QKnobs kn)
 {
     const int t = threadIdx.x, pos = t & 3;
     const uint64_t b0 = (uint64_t)blockIdx.x * (64 * kRowU) + (uint64_t)(t >> 2);
@@ -104,18 +130,22 @@ __global__ __launch_bounds__(256) void k_quant_row(const uint16_t *__restrict__ 
         widen8(raw[u], sg, v);
         uint32_t sc;
         const uint32_t w = quant8<GRID, ROUND, HN, 1, 2>(v, pos, b, kn, &sc);
-        store_slice<GRID, 1>(codes, scales, fmt, b, pos, w, sc, b < nblocks);
+        uint64_t line = 0, jb = b;
+        if (out.layout != MXQ_LAYOUT_ROWS) {
+            line = b / nbr;
+            jb = b - line * nbr;
+        }
+        if (out.layout == MXQ_LAYOUT_ROWS)
+            store_slice<GRID, 1>(out, 0, b, pos, w, sc, b < nblocks);   // line 0, block b == line*nbr+jb
+        else
+            store_slice<GRID, 1>(out, line, jb, pos, w, sc, b < nblocks);
     }
 }
 
 template <int GRID, int ROUND, int HN, bool ROWS, bool COLS>
 __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t ld,
-                                                    uint8_t *__restrict__ rcodes,
-                                                    uint8_t *__restrict__ rscales, int rfmt,
-                                                    uint8_t *__restrict__ ccodes,
-                                                    uint8_t *__restrict__ cscales, int cfmt,
-                                                    int vec, QKnobs kn)
+                                                    int64_t cols, int64_t ld, OutDesc rout,
+                                                    OutDesc cout, int vec, QKnobs kn)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int g = lane >> 4, l16 = lane & 15, qr = l16 & 3, qc = l16 >> 2;
@@ -159,7 +189,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
             const uint64_t blk = (uint64_t)c * nbc + jb;
             uint32_t sc;
             const uint32_t w = quant8<GRID, ROUND, HN, 1, 2>(v, qr, blk, kn, &sc);
-            store_slice<GRID, 1>(ccodes, cscales, cfmt, blk, qr, w, sc, c < cols);
+            store_slice<GRID, 1>(cout, (uint64_t)c, jb, qr, w, sc, c < cols);
         }
     }
     if constexpr (ROWS) {
@@ -174,7 +204,7 @@ __global__ __launch_bounds__(256) void k_quant_tile(const uint16_t *__restrict__
             const uint64_t blk = (uint64_t)(r0 + i) * nbr + jb;
             uint32_t sc;
             const uint32_t w = quant8<GRID, ROUND, HN, 4, 8>(v, qc, blk, kn, &sc);
-            store_slice<GRID, 4>(rcodes, rscales, rfmt, blk, qc, w, sc, c0 < cols);
+            store_slice<GRID, 4>(rout, (uint64_t)(r0 + i), jb, qc, w, sc, c0 < cols);
         }
     }
 }
@@ -208,10 +238,8 @@ namespace {
 struct QuantLaunch {
     const uint16_t *x;
     int64_t rows, cols, ld;
-    uint8_t *rcodes, *rscales;
-    int rfmt;
-    uint8_t *ccodes, *cscales;
-    int cfmt;
+    bool has_row, has_col;
+    OutDesc rout, cout;
     int vec;  // x 16-byte aligned and ld % 8 == 0: 128-bit loads
     QKnobs kn;
     hipStream_t s;
@@ -220,24 +248,22 @@ struct QuantLaunch {
 template <int GRID, int ROUND, int HN>
 hipError_t launch_quant(const QuantLaunch &q)
 {
-    const bool rows_out = q.rcodes != nullptr, cols_out = q.ccodes != nullptr;
+    const bool rows_out = q.has_row, cols_out = q.has_col;
     if (rows_out && !cols_out) {
         const uint64_t nbr = (uint64_t)q.cols / 32;
         const uint64_t nblocks = (uint64_t)q.rows * nbr;
         const uint64_t grid = (nblocks + 64 * kRowU - 1) / (64 * kRowU);
         hipLaunchKernelGGL((k_quant_row<GRID, ROUND, HN>), dim3((unsigned)grid), dim3(256), 0, q.s,
                            q.x, nblocks, (uint32_t)nbr, q.ld, (int)(q.ld == q.cols), q.vec,
-                           q.rcodes, q.rscales, q.rfmt, q.kn);
+                           q.rout, q.kn);
     } else {
         const dim3 grid((unsigned)((q.cols + 127) / 128), (unsigned)((q.rows + 127) / 128));
         if (rows_out)
             hipLaunchKernelGGL((k_quant_tile<GRID, ROUND, HN, true, true>), grid, dim3(256), 0, q.s,
-                               q.x, q.rows, q.cols, q.ld, q.rcodes, q.rscales, q.rfmt, q.ccodes,
-                               q.cscales, q.cfmt, q.vec, q.kn);
+                               q.x, q.rows, q.cols, q.ld, q.rout, q.cout, q.vec, q.kn);
         else
             hipLaunchKernelGGL((k_quant_tile<GRID, ROUND, HN, false, true>), grid, dim3(256), 0,
-                               q.s, q.x, q.rows, q.cols, q.ld, q.rcodes, q.rscales, q.rfmt,
-                               q.ccodes, q.cscales, q.cfmt, q.vec, q.kn);
+                               q.s, q.x, q.rows, q.cols, q.ld, q.rout, q.cout, q.vec, q.kn);
     }
     return hipGetLastError();
 }
@@ -269,15 +295,21 @@ mxq_status check_qconfig(const mxq_qconfig *cfg)
     return MXQ_OK;
 }
 
-mxq_status check_qtensor_out(const mxq_qtensor *t, int32_t grid)
+mxq_status check_qtensor_out(const mxq_qtensor *t, int32_t grid, int64_t k)
 {
     if (!t->codes || !t->scales)
         return MXQ_ERR_NULL;
     if (t->fmt != MXQ_FMT_FP4 && t->fmt != MXQ_FMT_E2M3)
         return MXQ_ERR_UNSUPPORTED;
+    if (t->layout != MXQ_LAYOUT_ROWS && t->layout != MXQ_LAYOUT_MFMA)
+        return MXQ_ERR_UNSUPPORTED;
     if (t->grid != grid)
         return MXQ_ERR_UNSUPPORTED;
-    if (reinterpret_cast<uintptr_t>(t->codes) % 4)
+    if (t->layout == MXQ_LAYOUT_MFMA && k % 128)
+        return MXQ_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(t->codes) % (t->layout == MXQ_LAYOUT_MFMA ? 16 : 4))
+        return MXQ_ERR_ALIGN;
+    if (t->layout == MXQ_LAYOUT_MFMA && reinterpret_cast<uintptr_t>(t->scales) % 4)
         return MXQ_ERR_ALIGN;
     return MXQ_OK;
 }
@@ -312,9 +344,9 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
         return MXQ_ERR_SHAPE;
     if (col_out && rows % 32)
         return MXQ_ERR_SHAPE;
-    if (row_out && (st = check_qtensor_out(row_out, cfg->grid)))
+    if (row_out && (st = check_qtensor_out(row_out, cfg->grid, cols)))
         return st;
-    if (col_out && (st = check_qtensor_out(col_out, cfg->grid)))
+    if (col_out && (st = check_qtensor_out(col_out, cfg->grid, rows)))
         return st;
     if (reinterpret_cast<uintptr_t>(x) % 2)
         return MXQ_ERR_ALIGN;
@@ -329,12 +361,16 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
     q.rows = rows;
     q.cols = cols;
     q.ld = ld_x;
-    q.rcodes = row_out ? static_cast<uint8_t *>(row_out->codes) : nullptr;
-    q.rscales = row_out ? row_out->scales : nullptr;
-    q.rfmt = row_out ? row_out->fmt : 0;
-    q.ccodes = col_out ? static_cast<uint8_t *>(col_out->codes) : nullptr;
-    q.cscales = col_out ? col_out->scales : nullptr;
-    q.cfmt = col_out ? col_out->fmt : 0;
+    q.has_row = row_out != nullptr;
+    q.has_col = col_out != nullptr;
+    q.rout = OutDesc{};
+    q.cout = OutDesc{};
+    if (row_out)
+        q.rout = OutDesc{static_cast<uint8_t *>(row_out->codes), row_out->scales, row_out->fmt,
+                         row_out->layout, (uint64_t)(cols / 32), (uint64_t)((rows + 15) / 16)};
+    if (col_out)
+        q.cout = OutDesc{static_cast<uint8_t *>(col_out->codes), col_out->scales, col_out->fmt,
+                         col_out->layout, (uint64_t)(rows / 32), (uint64_t)((cols + 15) / 16)};
     q.vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0 && ld_x % 8 == 0) ? 1 : 0;
     q.kn = make_knobs(cfg);
     q.s = static_cast<hipStream_t>(stream);

@@ -104,12 +104,421 @@ __global__ __launch_bounds__(256) void k_wgrad_simple(const uint8_t *__restrict_
         }
 }
 
+// ---- LDS-staged kernel -----------------------------------------------------
+// Workgroup tile 256 x 256 (4 waves of 128 x 128 = 8 x 8 MFMA tiles of
+// 16 x 16); one K step = 128 = 4 blocks per row.
+//
+// Block assignment: K steps come in groups of 4 (16 blocks = 512 K).  At step
+// s' of group q, lane group g takes block 16 q + 4 g + s'.  A lane's 4 scale
+// bytes for the group are then the contiguous dword at scales[row][16 q + 4 g],
+// with byte s' for step s'; A and B use the same assignment, so the product is
+// unchanged (only the fp32 summation order depends on it).
+//
+// Staging: operand bytes go from global memory straight into LDS with
+// global_load_lds, which writes lane L's 16 (dwordx4) or 12 (dwordx3) bytes at
+// 16 L.  Layout "fragment-major": for each 16-row tile, fragment lane
+// l = 16 g + r's block bytes sit at 16 l -- one 1 KB region for an FP4 block,
+// two (bytes 0-11 and 12-23) for an FP6 block -- so every fragment read is a
+// contiguous, bank-conflict-free 128-bit sweep.  Two stages alternate: the next step's loads are
+// in flight during this step's MFMAs.  Scales are staged per group, [row][16 B].
+constexpr int kBM = 256, kBN = 256;
+
+template <int F> constexpr int blk_bytes() { return F == kMfmaFP4 ? 16 : 24; }
+
+template <int F> constexpr int tile_bytes() { return F == kMfmaFP4 ? 1024 : 2048; }
+
+template <int FA, int FB>
+constexpr int lds_bytes() { return 2 * 16 * (tile_bytes<FA>() + tile_bytes<FB>()) + 2 * 2 * 4096; }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef const __attribute__((address_space(1))) void glb_void;
+
+__device__ __forceinline__ void g2l16(const uint8_t *g, uint8_t *l)
+{
+    __builtin_amdgcn_global_load_lds((glb_void *)g, (lds_void *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void g2l12(const uint8_t *g, uint8_t *l)
+{
+    __builtin_amdgcn_global_load_lds((glb_void *)g, (lds_void *)l, 12, 0, 0);
+}
+
+// This wave's share (4 of the 16 row tiles) of one operand's K step.
+template <int F>
+__device__ __forceinline__ void stage_step(const uint8_t *__restrict__ codes, int64_t row0,
+                                           int64_t rows, int64_t nbk, int64_t q, int sp,
+                                           uint8_t *lds_stage, int wv, int lane)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int rt = 4 * wv + i;
+        if constexpr (F == kMfmaFP4) {
+            const int g = lane >> 4, rr = lane & 15;
+            const int64_t rg = min(row0 + 16 * rt + rr, rows - 1);
+            g2l16(codes + (rg * nbk + 16 * q + 4 * g + sp) * 16, lds_stage + rt * 1024);
+        } else {
+            const int g = lane >> 4, rr = lane & 15;
+            const int64_t rg = min(row0 + 16 * rt + rr, rows - 1);
+            const uint8_t *src = codes + (rg * nbk + 16 * q + 4 * g + sp) * 24;
+            g2l12(src, lds_stage + rt * 2048);
+            g2l12(src + 12, lds_stage + rt * 2048 + 1024);
+        }
+    }
+}
+
+// This wave's 64 rows of one operand's scale group (16 bytes per row).
+__device__ __forceinline__ void stage_scales(const uint8_t *__restrict__ scales, int64_t row0,
+                                             int64_t rows, int64_t nbk, int64_t q, uint8_t *lds,
+                                             int wv, int lane)
+{
+    const int64_t rg = min(row0 + 64 * wv + lane, rows - 1);
+    g2l16(scales + rg * nbk + 16 * q, lds + 64 * wv * 16);
+}
+
+template <int F>
+__device__ __forceinline__ v8i lds_fragment(const uint8_t *__restrict__ lds, int rt, int lane)
+{
+    v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (F == kMfmaFP4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(lds + rt * 1024 + lane * 16);
+        r[0] = (int)q.x; r[1] = (int)q.y; r[2] = (int)q.z; r[3] = (int)q.w;
+    } else {
+        const uint4 a = *reinterpret_cast<const uint4 *>(lds + rt * 2048 + lane * 16);
+        const uint4 b = *reinterpret_cast<const uint4 *>(lds + rt * 2048 + 1024 + lane * 16);
+        r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)a.z;
+        r[3] = (int)b.x; r[4] = (int)b.y; r[5] = (int)b.z;
+    }
+    return r;
+}
+
+// Tile order: workgroups go round-robin over the 8 XCDs; give each XCD a
+// contiguous run of tiles, grouped 4 tile-rows deep, so the tiles sharing an
+// XCD's L2 share A and B panels.
+__device__ __forceinline__ void tile_of(int w, int ntm, int ntn, int &tm, int &tn)
+{
+    const int total = ntm * ntn;
+    if (total % 8 == 0)
+        w = (w % 8) * (total / 8) + w / 8;
+    constexpr int GM = 4;
+    const int gsize = GM * ntn;
+    const int grp = w / gsize;
+    const int first = grp * GM;
+    const int gm = min(ntm - first, GM);
+    const int loc = w - grp * gsize;
+    tm = first + loc % gm;
+    tn = loc / gm;
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(256, 1) void k_wgrad_lds(const uint8_t *__restrict__ ac,
+                                                      const uint8_t *__restrict__ as,
+                                                      const uint8_t *__restrict__ bc,
+                                                      const uint8_t *__restrict__ bs, int64_t m,
+                                                      int64_t n, int64_t k, float *__restrict__ c,
+                                                      int64_t ldc)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int SA = 16 * tile_bytes<FA>(), SB = 16 * tile_bytes<FB>();
+    constexpr int STAGE = SA + SB;
+    uint8_t *const scl = smem + 2 * STAGE;     // [2 groups][A 4 KB | B 4 KB]
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int wm = wv >> 1, wn = wv & 1, g = lane >> 4, li = lane & 15;
+    int tm, tn;
+    tile_of(blockIdx.x, (int)((m + kBM - 1) / kBM), (int)((n + kBN - 1) / kBN), tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    const int64_t nbk = k / 32, nsteps = k / 128;
+
+    v4f acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // prologue: scales of group 0, operands of step 0
+    stage_scales(as, m0, m, nbk, 0, scl, wv, lane);
+    stage_scales(bs, n0, n, nbk, 0, scl + 4096, wv, lane);
+    stage_step<FA>(ac, m0, m, nbk, 0, 0, smem, wv, lane);
+    stage_step<FB>(bc, n0, n, nbk, 0, 0, smem + SA, wv, lane);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    uint32_t sca[8], scb[8];
+    for (int64_t s = 0; s < nsteps; ++s) {
+        const int cur = (int)(s & 1);
+        const int64_t q = s >> 2;
+        const int sp = (int)(s & 3);
+        if (s + 1 < nsteps) {
+            const int64_t q1 = (s + 1) >> 2;
+            const int sp1 = (int)((s + 1) & 3);
+            uint8_t *nxt = smem + (cur ^ 1) * STAGE;
+            stage_step<FA>(ac, m0, m, nbk, q1, sp1, nxt, wv, lane);
+            stage_step<FB>(bc, n0, n, nbk, q1, sp1, nxt + SA, wv, lane);
+        }
+        if (sp == 0) {
+            const uint8_t *sgA = scl + (q & 1) * 8192, *sgB = sgA + 4096;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sca[i] = *reinterpret_cast<const uint32_t *>(sgA + (128 * wm + 16 * i + li) * 16 + 4 * g);
+                scb[i] = *reinterpret_cast<const uint32_t *>(sgB + (128 * wn + 16 * i + li) * 16 + 4 * g);
+            }
+            if (4 * (q + 1) < nsteps) {
+                // the other group buffer was last read at step 4 (q - 1)
+                uint8_t *sg1 = scl + ((q + 1) & 1) * 8192;
+                stage_scales(as, m0, m, nbk, q + 1, sg1, wv, lane);
+                stage_scales(bs, n0, n, nbk, q + 1, sg1 + 4096, wv, lane);
+            }
+        }
+        const uint8_t *stg = smem + cur * STAGE;
+        const int sh = 8 * sp;
+        v8i bf[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            bf[j] = lds_fragment<FB>(stg + SA, 8 * wn + j, lane);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const v8i af = lds_fragment<FA>(stg, 8 * wm + i, lane);
+            const int sai = (int)((sca[i] >> sh) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af, bf[j], acc[i][j], FA, FB, 0, sai, 0, (int)((scb[j] >> sh) & 0xFFu));
+        }
+        __builtin_amdgcn_s_waitcnt(0);   // this wave's loads into the other stage landed
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t col = n0 + 128 * wn + 16 * j + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + 128 * wm + 16 * i + 4 * g + r;
+                if (row < m && col < n)
+                    c[row * ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
+// ---- MFMA-tiled operands -----------------------------------------------------
+// Both operands in MXQ_LAYOUT_MFMA: a K step of one 16-row tile is one
+// contiguous 1 KB (FP4) or 1.5 KB (FP6) fragment, already in lane order, and
+// the 16 tiles a workgroup needs for a step are adjacent.  8 waves (2 per
+// SIMD) of 128 x 64 output each cover a 256 x 256 tile.  The step's operand
+// bytes are copied verbatim into LDS with 16-byte direct loads (lane order ==
+// memory order), issued one step ahead into a second buffer.  The copies are
+// issued from inline asm so the compiler, which cannot tell them apart from
+// the buffer being read, does not drain them before every LDS read; their
+// completion is awaited explicitly (vmcnt) before the barrier that publishes
+// the buffer.  A lane's 4 scale bytes per 4-step group come straight from
+// global memory, one dword per fragment row, a group ahead.
+constexpr int kWaves = 8;
+
+__device__ __forceinline__ void dma16(const uint8_t *g, const uint8_t *l)
+{
+    const uint32_t la = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t *)l);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(la))
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ void wait_all_vm()
+{
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+}
+
+__device__ __forceinline__ void barrier_no_fence()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int F>
+__device__ __forceinline__ v8i tiled_fragment(const uint8_t *__restrict__ lds, int rt, int lane)
+{
+    v8i r = {0, 0, 0, 0, 0, 0, 0, 0};
+    if constexpr (F == kMfmaFP4) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(lds + rt * 1024 + lane * 16);
+        r[0] = (int)q.x; r[1] = (int)q.y; r[2] = (int)q.z; r[3] = (int)q.w;
+    } else {
+        const uint2 *p = reinterpret_cast<const uint2 *>(lds + rt * 1536 + lane * 24);
+        const uint2 a = p[0], b = p[1], c = p[2];
+        r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)b.x;
+        r[3] = (int)b.y; r[4] = (int)c.x; r[5] = (int)c.y;
+    }
+    return r;
+}
+
+// Copy this wave's share of one operand's step (16 tiles x 64 x BB bytes,
+// i.e. BB chunks of 1 KB) into LDS.  Tiles past the operand's last tile are
+// clamped to it (their rows are never stored).
+template <int F>
+__device__ __forceinline__ void tiled_stage(const uint8_t *__restrict__ codes, int64_t ntiles,
+                                            int64_t t0, int64_t s, uint8_t *lds, int chunk0,
+                                            int nchunks, int lane)
+{
+    constexpr int BB = blk_bytes<F>(), TB = 64 * BB;
+    const uint8_t *stepbase = codes + s * ntiles * TB;
+    for (int i = 0; i < nchunks; ++i) {
+        const int ch = chunk0 + i;
+        const int o = ch * 1024 + lane * 16;          // byte within the 16-tile run
+        const int64_t tile = min(t0 + o / TB, ntiles - 1);
+        dma16(stepbase + tile * TB + (o % TB), lds + ch * 1024);
+    }
+}
+
+template <int FA, int FB>
+constexpr int tiled_lds_bytes() { return 2 * 16 * 64 * (blk_bytes<FA>() + blk_bytes<FB>()); }
+
+template <int FA, int FB>
+__global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_tiled(const uint8_t *__restrict__ ac,
+                                                                const uint8_t *__restrict__ as,
+                                                                const uint8_t *__restrict__ bc,
+                                                                const uint8_t *__restrict__ bs,
+                                                                int64_t m, int64_t n, int64_t k,
+                                                                float *__restrict__ c, int64_t ldc)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int SA = 16 * 64 * blk_bytes<FA>(), SB = 16 * 64 * blk_bytes<FB>();
+    constexpr int STAGE = SA + SB;
+    constexpr int CA = SA / 1024, CB = SB / 1024;          // 1 KB chunks per operand
+    constexpr int PER = (CA + CB) / kWaves;                // chunks per wave per step
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int wm = wv >> 2, wn = wv & 3, g = lane >> 4, li = lane & 15;
+    int tm, tn;
+    tile_of(blockIdx.x, (int)((m + kBM - 1) / kBM), (int)((n + kBN - 1) / kBN), tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    const int64_t ntA = (m + 15) / 16, ntB = (n + 15) / 16;
+    const int64_t nsteps = k / 128;
+
+    // this wave's chunks: a contiguous run over [A chunks | B chunks]
+    const int c0 = wv * PER;
+    auto stage = [&](int64_t s, uint8_t *buf) {
+        const int a_lo = c0, a_hi = min(c0 + PER, CA);
+        if (a_hi > a_lo)
+            tiled_stage<FA>(ac, ntA, m0 / 16, s, buf, a_lo, a_hi - a_lo, lane);
+        const int b_lo = max(c0, CA) - CA, b_hi = c0 + PER - CA;
+        if (b_hi > b_lo)
+            tiled_stage<FB>(bc, ntB, n0 / 16, s, buf + SA, b_lo, b_hi - b_lo, lane);
+    };
+    const uint32_t *sA = reinterpret_cast<const uint32_t *>(as);
+    const uint32_t *sB = reinterpret_cast<const uint32_t *>(bs);
+    uint32_t ca[8], cb[4], na[8], nb[4];
+    auto scales = [&](int64_t q, uint32_t (&xa)[8], uint32_t (&xb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t tile = min(m0 / 16 + 8 * wm + i, ntA - 1);
+            xa[i] = sA[(q * ntA + tile) * 64 + lane];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t tile = min(n0 / 16 + 4 * wn + j, ntB - 1);
+            xb[j] = sB[(q * ntB + tile) * 64 + lane];
+        }
+    };
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    scales(0, ca, cb);
+    stage(0, smem);
+    for (int64_t s = 0; s < nsteps; ++s) {
+        const int cur = (int)(s & 1);
+        wait_all_vm();                 // this wave's copies for step s (and scale loads) landed
+        barrier_no_fence();            // ... and everyone's; step s-1's buffer is free
+        if ((s & 3) == 0 && s > 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ca[i] = na[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                cb[j] = nb[j];
+        }
+        if (s + 1 < nsteps)
+            stage(s + 1, smem + (cur ^ 1) * STAGE);
+        if ((s & 3) == 0 && 4 * (s / 4 + 1) < nsteps)
+            scales(s / 4 + 1, na, nb);
+        const uint8_t *st = smem + cur * STAGE;
+        const int sh = 8 * (int)(s & 3);
+        v8i bf[4];
+        int sb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf[j] = tiled_fragment<FB>(st + SA, 4 * wn + j, lane);
+            sb[j] = (int)((cb[j] >> sh) & 0xFFu);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const v8i af = tiled_fragment<FA>(st, 8 * wm + i, lane);
+            const int sa = (int)((ca[i] >> sh) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af, bf[j], acc[i][j], FA, FB, 0, sa, 0, sb[j]);
+        }
+    }
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + 64 * wn + 16 * j + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + 128 * wm + 16 * i + 4 * g + r;
+                if (row < m && col < n)
+                    c[row * ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
 __global__ __launch_bounds__(256) void k_zero_fill(float *__restrict__ c, int64_t m, int64_t n,
                                                    int64_t ldc)
 {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < m * n)
         c[(i / n) * ldc + (i % n)] = 0.0f;
+}
+
+template <int FA, int FB>
+hipError_t launch_staged(int64_t tiles, hipStream_t s, const uint8_t *ac, const uint8_t *as,
+                         const uint8_t *bc, const uint8_t *bs, int64_t m, int64_t n, int64_t k,
+                         float *c, int64_t ldc)
+{
+    constexpr int lds = lds_bytes<FA, FB>();
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_wgrad_lds<FA, FB>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((k_wgrad_lds<FA, FB>), dim3((unsigned)tiles), dim3(256), lds, s, ac, as, bc,
+                       bs, m, n, k, c, ldc);
+    return hipGetLastError();
+}
+
+template <int FA, int FB>
+hipError_t launch_tiled(int64_t tiles, hipStream_t s, const uint8_t *ac, const uint8_t *as,
+                        const uint8_t *bc, const uint8_t *bs, int64_t m, int64_t n, int64_t k,
+                        float *c, int64_t ldc)
+{
+    constexpr int lds = tiled_lds_bytes<FA, FB>();
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&k_wgrad_tiled<FA, FB>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (attr != hipSuccess)
+        return attr;
+    hipLaunchKernelGGL((k_wgrad_tiled<FA, FB>), dim3((unsigned)tiles), dim3(64 * kWaves), lds, s,
+                       ac, as, bc, bs, m, n, k, c, ldc);
+    return hipGetLastError();
 }
 
 namespace {
@@ -137,6 +546,12 @@ extern "C" mxq_status mxq_wgrad_gemm(const mxq_qtensor *a, const mxq_qtensor *b,
         return MXQ_ERR_UNSUPPORTED;
     if (m < 0 || n < 0 || k < 0 || k % 128 || ldc < n)
         return MXQ_ERR_SHAPE;
+    if ((a->layout != MXQ_LAYOUT_ROWS && a->layout != MXQ_LAYOUT_MFMA) || a->layout != b->layout)
+        return MXQ_ERR_UNSUPPORTED;
+    if (a->layout == MXQ_LAYOUT_MFMA &&
+        (reinterpret_cast<uintptr_t>(a->codes) % 16 || reinterpret_cast<uintptr_t>(b->codes) % 16 ||
+         reinterpret_cast<uintptr_t>(a->scales) % 4 || reinterpret_cast<uintptr_t>(b->scales) % 4))
+        return MXQ_ERR_ALIGN;
     if (reinterpret_cast<uintptr_t>(a->codes) % 8 || reinterpret_cast<uintptr_t>(b->codes) % 8 ||
         reinterpret_cast<uintptr_t>(c) % 4)
         return MXQ_ERR_ALIGN;
@@ -154,9 +569,44 @@ extern "C" mxq_status mxq_wgrad_gemm(const mxq_qtensor *a, const mxq_qtensor *b,
                            m, n, ldc);
         return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
     }
-    const dim3 grid((unsigned)((n + kTN - 1) / kTN), (unsigned)((m + kTM - 1) / kTM));
     const uint8_t *ac = static_cast<const uint8_t *>(a->codes);
     const uint8_t *bc = static_cast<const uint8_t *>(b->codes);
+    if (a->layout == MXQ_LAYOUT_MFMA) {
+        const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
+        if (tiles > 0x7FFFFFFF)
+            return MXQ_ERR_SHAPE;
+        hipError_t e;
+        if (fa == kMfmaFP4 && fb == kMfmaFP4)
+            e = launch_tiled<kMfmaFP4, kMfmaFP4>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        else if (fa == kMfmaFP6 && fb == kMfmaFP6)
+            e = launch_tiled<kMfmaFP6, kMfmaFP6>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        else if (fa == kMfmaFP4)
+            e = launch_tiled<kMfmaFP4, kMfmaFP6>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        else
+            e = launch_tiled<kMfmaFP6, kMfmaFP4>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        return e == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
+    }
+    const bool staged = k % 512 == 0 && reinterpret_cast<uintptr_t>(ac) % 16 == 0 &&
+                        reinterpret_cast<uintptr_t>(bc) % 16 == 0 &&
+                        reinterpret_cast<uintptr_t>(a->scales) % 16 == 0 &&
+                        reinterpret_cast<uintptr_t>(b->scales) % 16 == 0;
+    if (staged) {
+        const int64_t tiles = ((m + kBM - 1) / kBM) * ((n + kBN - 1) / kBN);
+        if (tiles > 0x7FFFFFFF)
+            return MXQ_ERR_SHAPE;
+        hipError_t e;
+        if (fa == kMfmaFP4 && fb == kMfmaFP4)
+            e = launch_staged<kMfmaFP4, kMfmaFP4>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        else if (fa == kMfmaFP6 && fb == kMfmaFP6)
+            e = launch_staged<kMfmaFP6, kMfmaFP6>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        else if (fa == kMfmaFP4)
+            e = launch_staged<kMfmaFP4, kMfmaFP6>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        else
+            e = launch_staged<kMfmaFP6, kMfmaFP4>(tiles, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
+        return e == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
+    }
+    // other K (multiples of 128) or alignments: direct loads, no LDS
+    const dim3 grid((unsigned)((n + kTN - 1) / kTN), (unsigned)((m + kTM - 1) / kTM));
     if (fa == kMfmaFP4 && fb == kMfmaFP4)
         hipLaunchKernelGGL((k_wgrad_simple<kMfmaFP4, kMfmaFP4>), grid, dim3(256), 0, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
     else if (fa == kMfmaFP6 && fb == kMfmaFP6)

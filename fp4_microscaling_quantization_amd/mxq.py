@@ -17,6 +17,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_UNSUPPORTED, ERR_DEVICE, ERR_WORKSPACE =
 GRID_E2M1, GRID_E1M2 = 0, 1
 RTNE, SR = 0, 1
 FMT_FP4, FMT_E2M3 = 0, 1
+LAYOUT_ROWS, LAYOUT_MFMA = 0, 1
 AXIS_ROW, AXIS_COL = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 
@@ -33,7 +34,7 @@ class QConfig(C.Structure):
 
 class QTensor(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("fmt", C.c_int32),
-                ("grid", C.c_int32)]
+                ("grid", C.c_int32), ("layout", C.c_int32)]
 
 
 class Stats(C.Structure):
@@ -109,29 +110,54 @@ def block_bytes(fmt: int) -> int:
     return 16 if fmt == FMT_FP4 else 24
 
 
-def empty_qtensor(lines: int, k: int, fmt: int, device):
-    """Device buffers for a [lines x k] block-quantized tensor: (codes, scales)."""
+def qtensor_sizes(lines: int, k: int, fmt: int, layout: int = LAYOUT_ROWS):
+    """(code bytes, scale bytes) of a [lines x k] block-quantized tensor."""
+    nb = k // 32
+    if layout == LAYOUT_ROWS:
+        return lines * nb * block_bytes(fmt), lines * nb
+    ntiles = (lines + 15) // 16
+    nsteps = k // 128
+    return nsteps * ntiles * 64 * block_bytes(fmt), ((nsteps + 3) // 4) * ntiles * 256
+
+
+def empty_qtensor(lines: int, k: int, fmt: int, device, layout: int = LAYOUT_ROWS, fill=None):
+    """Device buffers (codes, scales): 2-D [lines, ...] for the row layout,
+    1-D byte arrays for the MFMA layout."""
     import torch
     nb = k // 32
-    codes = torch.empty((lines, nb * block_bytes(fmt)), dtype=torch.uint8, device=device)
-    scales = torch.empty((lines, nb), dtype=torch.uint8, device=device)
+    if layout == LAYOUT_ROWS:
+        codes = torch.empty((lines, nb * block_bytes(fmt)), dtype=torch.uint8, device=device)
+        scales = torch.empty((lines, nb), dtype=torch.uint8, device=device)
+    else:
+        cb, sb = qtensor_sizes(lines, k, fmt, layout)
+        codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        scales = torch.empty(sb, dtype=torch.uint8, device=device)
+    if fill is not None:
+        codes.fill_(fill)
+        scales.fill_(fill)
     return codes, scales
 
 
-def qtensor(codes, scales, fmt: int, grid: int) -> QTensor:
-    return QTensor(codes.data_ptr(), scales.data_ptr(), fmt, grid)
+def qtensor(codes, scales, fmt: int, grid: int, layout: int = LAYOUT_ROWS) -> QTensor:
+    return QTensor(codes.data_ptr(), scales.data_ptr(), fmt, grid, layout)
 
 
 # ---- entry points ---------------------------------------------------------
 
 def quantize_into(cfg: QConfig, x, row=None, col=None, rows=None, cols=None, ld=None,
                   stream=None):
-    """mxq_quantize on caller-owned buffers.  row/col: (codes, scales, fmt) or None."""
+    """mxq_quantize on caller-owned buffers.
+    row/col: (codes, scales, fmt) or (codes, scales, fmt, layout), or None."""
     rows = x.shape[0] if rows is None else rows
     cols = x.shape[1] if cols is None else cols
     ld = x.stride(0) if ld is None else ld
-    rt = QTensor(row[0].data_ptr(), row[1].data_ptr(), row[2], cfg.grid) if row else None
-    ct = QTensor(col[0].data_ptr(), col[1].data_ptr(), col[2], cfg.grid) if col else None
+
+    def desc(o):
+        if not o:
+            return None
+        lay = o[3] if len(o) > 3 else LAYOUT_ROWS
+        return QTensor(o[0].data_ptr(), o[1].data_ptr(), o[2], cfg.grid, lay)
+    rt, ct = desc(row), desc(col)
     st = lib().mxq_quantize(C.byref(cfg), _ptr(x), rows, cols, ld,
                             C.byref(rt) if rt else None, C.byref(ct) if ct else None,
                             _stream(stream))
@@ -139,46 +165,52 @@ def quantize_into(cfg: QConfig, x, row=None, col=None, rows=None, cols=None, ld=
 
 
 def quantize(x, grid=GRID_E2M1, round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
-             sr_bits=16, row=True, col=False, row_fmt=FMT_FP4, col_fmt=FMT_FP4, stream=None):
+             sr_bits=16, row=True, col=False, row_fmt=FMT_FP4, col_fmt=FMT_FP4,
+             row_layout=LAYOUT_ROWS, col_layout=LAYOUT_ROWS, fill=None, stream=None):
     """Quantize a 2-D bf16 CUDA tensor; returns {'row': (codes, scales), 'col': (...)}."""
     cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits)
     rows, cols = x.shape
     out = {}
     r = c = None
     if row:
-        rc, rs = empty_qtensor(rows, cols, row_fmt, x.device)
-        r = (rc, rs, row_fmt)
+        rc, rs = empty_qtensor(rows, cols, row_fmt, x.device, row_layout, fill)
+        r = (rc, rs, row_fmt, row_layout)
         out["row"] = (rc, rs)
     if col:
-        cc, cs = empty_qtensor(cols, rows, col_fmt, x.device)
-        c = (cc, cs, col_fmt)
+        cc, cs = empty_qtensor(cols, rows, col_fmt, x.device, col_layout, fill)
+        c = (cc, cs, col_fmt, col_layout)
         out["col"] = (cc, cs)
     quantize_into(cfg, x, r, c, stream=stream)
     return out
 
 
-def dequantize(codes, scales, fmt: int, grid: int, out_dtype=OUT_F32, stream=None):
+def dequantize(codes, scales, fmt: int, grid: int, out_dtype=OUT_F32, layout=LAYOUT_ROWS,
+               lines=None, k=None, stream=None):
     import torch
-    lines = scales.shape[0]
-    k = scales.shape[1] * 32
+    if layout == LAYOUT_ROWS:
+        lines = scales.shape[0] if lines is None else lines
+        k = scales.shape[1] * 32 if k is None else k
     dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
     out = torch.empty((lines, k), dtype=dt, device=codes.device)
-    q = qtensor(codes, scales, fmt, grid)
+    q = qtensor(codes, scales, fmt, grid, layout)
     _check("mxq_dequantize", lib().mxq_dequantize(C.byref(q), lines, k, out_dtype, _ptr(out), k,
                                                   _stream(stream)))
     return out
 
 
 def wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid, out=None,
-               stream=None):
-    """C [m x n] fp32 = A [m x k] B [n x k]^T on block-quantized operands."""
+               layout=LAYOUT_ROWS, m=None, n=None, k=None, stream=None):
+    """C [m x n] fp32 = A [m x k] B [n x k]^T on block-quantized operands (both
+    in `layout`; m, n, k are required for the MFMA layout)."""
     import torch
-    m, n = a_scales.shape[0], b_scales.shape[0]
-    k = a_scales.shape[1] * 32
-    assert b_scales.shape[1] * 32 == k
+    if layout == LAYOUT_ROWS:
+        m = a_scales.shape[0] if m is None else m
+        n = b_scales.shape[0] if n is None else n
+        k = a_scales.shape[1] * 32 if k is None else k
+        assert b_scales.shape[1] * 32 == k
     c = torch.empty((m, n), dtype=torch.float32, device=a_codes.device) if out is None else out
-    qa = qtensor(a_codes, a_scales, a_fmt, a_grid)
-    qb = qtensor(b_codes, b_scales, b_fmt, b_grid)
+    qa = qtensor(a_codes, a_scales, a_fmt, a_grid, layout)
+    qb = qtensor(b_codes, b_scales, b_fmt, b_grid, layout)
     _check("mxq_wgrad_gemm", lib().mxq_wgrad_gemm(C.byref(qa), C.byref(qb), m, n, k, _ptr(c),
                                                   c.stride(0), _stream(stream)))
     return c

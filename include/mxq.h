@@ -76,6 +76,22 @@ typedef int32_t mxq_status;
 #define MXQ_FMT_FP4 0
 #define MXQ_FMT_E2M3 1
 
+/* Placement of a block-quantized tensor's blocks in memory:
+ *   MXQ_LAYOUT_ROWS:  codes [lines][k/32][block bytes], scales [lines][k/32].
+ *   MXQ_LAYOUT_MFMA:  the operand order of the 16x16x128 block-scaled matrix
+ *                     cores, so a GEMM streams each operand contiguously.
+ *                     With T = ceil(lines/16) tiles of 16 lines, K steps of 4
+ *                     blocks (s = b / 4) and lane l = 16 g + r for block
+ *                     4 s + g of line 16 t + r:
+ *                       codes  [k/128 steps][T][64 lanes][block bytes],
+ *                       scales [ceil(k/512) groups][T][64 lanes][4 bytes],
+ *                     byte j of a lane's scale word is the scale of step
+ *                     4 q + j of group q.  Needs k % 128 == 0.  The bytes of
+ *                     padding lines (lines..16T-1) and of absent steps in a
+ *                     last partial group are never written or read. */
+#define MXQ_LAYOUT_ROWS 0
+#define MXQ_LAYOUT_MFMA 1
+
 #define MXQ_AXIS_ROW 0          /* blocks run along the last (contiguous) dim */
 #define MXQ_AXIS_COL 1          /* blocks run along the first dim; transposed */
 
@@ -108,14 +124,16 @@ typedef struct {
 } mxq_qconfig;
 
 /* A block-quantized tensor of `lines` lines, each `k` elements long (k % 32
- * == 0), stored densely: codes [lines][k/32][16 or 24 bytes], scales
- * [lines][k/32] E8M0 bytes (value 2^(s-127); 0xFF marks a non-finite block).
- * codes must be 4-byte aligned. */
+ * == 0): 16 (FP4) or 24 (E2M3) code bytes and one E8M0 scale byte (value
+ * 2^(s-127); 0xFF marks a non-finite block) per 32-element block, placed as
+ * `layout` says.  codes must be 4-byte aligned (16-byte for MXQ_LAYOUT_MFMA,
+ * whose scales must be 4-byte aligned). */
 typedef struct {
     void *codes;
     uint8_t *scales;
-    int32_t fmt;   /* MXQ_FMT_* */
-    int32_t grid;  /* MXQ_GRID_* of the stored values */
+    int32_t fmt;     /* MXQ_FMT_* */
+    int32_t grid;    /* MXQ_GRID_* of the stored values */
+    int32_t layout;  /* MXQ_LAYOUT_* */
 } mxq_qtensor;
 
 /* Shrinkage-bias / SQNR sums over the rotated values y of the blocks with a

@@ -464,3 +464,31 @@ int orc_stats(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axi
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Operand placement of the 16x16x128 block-scaled matrix cores.  A pure    */
+/* byte permutation of the row layout, no arithmetic: K steps of 4 blocks,  */
+/* tiles of 16 lines; block 4 s + g of line 16 t + r is lane 16 g + r of    */
+/* fragment (s, t); the scale of step s sits in byte s % 4 of that lane's   */
+/* word in scale group s / 4.  Untouched bytes keep their prior contents.  */
+/* ------------------------------------------------------------------------ */
+int orc_to_mfma_layout(const uint8_t *codes, const uint8_t *scales, int64_t lines, int64_t k,
+                       int fmt, uint8_t *tcodes, uint8_t *tscales)
+{
+    if (lines < 0 || k < 0 || k % 128)
+        return -1;
+    int64_t nbk = k / 32;
+    int64_t ntiles = (lines + 15) / 16;
+    int64_t bb = fmt == ORC_FMT_FP4 ? 16 : 24;
+    for (int64_t line = 0; line < lines; ++line) {
+        for (int64_t jb = 0; jb < nbk; ++jb) {
+            int64_t step = jb / 4, g = jb % 4, tile = line / 16, r = line % 16;
+            int64_t lane = 16 * g + r;
+            int64_t dst = (step * ntiles + tile) * 64 + lane;
+            memcpy(tcodes + dst * bb, codes + (line * nbk + jb) * bb, (size_t)bb);
+            int64_t group = step / 4;
+            tscales[((group * ntiles + tile) * 64 + lane) * 4 + step % 4] = scales[line * nbk + jb];
+        }
+    }
+    return 0;
+}

@@ -111,6 +111,11 @@ int orc_quantize_lines(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld
                        const orc_qparams *p, int fmt, int64_t line0, uint8_t *codes,
                        uint8_t *scales);
 
+/* Row layout -> the 16x16x128 matrix-core operand layout (a byte permutation;
+ * bytes of padding lines / absent steps are left untouched). k % 128 == 0. */
+int orc_to_mfma_layout(const uint8_t *codes, const uint8_t *scales, int64_t lines, int64_t k,
+                       int fmt, uint8_t *tcodes, uint8_t *tscales);
+
 /* Dequantize [lines x k] blocks (k along the block axis) to fp64. */
 int orc_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t lines, int64_t k,
                    int grid, int fmt, double *out);

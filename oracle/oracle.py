@@ -84,6 +84,7 @@ def lib():
         L.orc_quantize_lines.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int,
                                          i64, P, P]
         L.orc_dequantize.argtypes = [P, P, i64, i64, C.c_int, C.c_int, P]
+        L.orc_to_mfma_layout.argtypes = [P, P, i64, i64, C.c_int, P, P]
         L.orc_gemm_abt_f64.argtypes = [P, P, i64, i64, i64, P]
         L.orc_stats.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int, P, P,
                                 C.POINTER(Stats)]
@@ -212,6 +213,27 @@ def quantize_lines(x, axis: int, p: QParams, line0: int, nlines: int, fmt: int =
     if rc != 0:
         raise ValueError("oracle quantize_lines rejected shape")
     return codes, scales
+
+
+def mfma_layout_sizes(lines: int, k: int, fmt: int):
+    ntiles = (lines + 15) // 16
+    nsteps = k // 128
+    return nsteps * ntiles * 64 * block_bytes(fmt), ((nsteps + 3) // 4) * ntiles * 256
+
+
+def to_mfma_layout(codes: np.ndarray, scales: np.ndarray, fmt: int, fill: int = 0):
+    """Row-layout (codes, scales) -> flat MFMA-layout byte arrays (prefilled with `fill`)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    lines, nblk = scales.shape
+    k = nblk * 32
+    cb, sb = mfma_layout_sizes(lines, k, fmt)
+    tc = np.full(cb, fill, dtype=np.uint8)
+    ts = np.full(sb, fill, dtype=np.uint8)
+    rc = lib().orc_to_mfma_layout(_ptr(codes), _ptr(scales), lines, k, fmt, _ptr(tc), _ptr(ts))
+    if rc != 0:
+        raise ValueError("oracle layout: k must be a multiple of 128")
+    return tc, ts
 
 
 def dequantize(codes: np.ndarray, scales: np.ndarray, grid: int, fmt: int = FMT_FP4) -> np.ndarray:

@@ -191,3 +191,90 @@ def test_sr_unbiased_over_64_seeds(orc):
     assert abs(mean) <= 0.5 * 2.0 ** -17 + 5 * sigma
     print(f"SR mean normalized error {mean:.3e} (sigma bound {sigma:.1e}); "
           f"RTNE {tot_rtne / n_unsat:.3e}")
+
+
+def _tiled(orc, codes, scales, fmt):
+    tc, ts = orc.to_mfma_layout(codes, scales, fmt, fill=0)
+    return _t(tc), _t(ts)
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 512), (100, 72, 384), (300, 520, 1152), (16, 16, 128)])
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: f"A{c[0]}B{c[1]}")
+def test_gemm_mfma_layout_exact_at_unit_scale(orc, shape, combo):
+    from fp4_microscaling_quantization_amd import mxq
+    m, n, k = shape
+    (fa, ga), (fb, gb) = combo
+    g = np.random.Generator(np.random.PCG64(m + 7 * n + k))
+    ac, as_ = _rand_codes(g, m, k, fa, ga, orc)
+    bc, bs = _rand_codes(g, n, k, fb, gb, orc)
+    say("gemm tiled exact", shape, combo)
+    ta, tas = _tiled(orc, ac, as_, fa)
+    tb, tbs = _tiled(orc, bc, bs, fb)
+    c = host(mxq.wgrad_gemm(ta, tas, fa, ga, tb, tbs, fb, gb, layout=mxq.LAYOUT_MFMA, m=m, n=n, k=k))
+    ref = orc.gemm_abt_f64(orc.dequantize(ac, as_, ga, fa), orc.dequantize(bc, bs, gb, fb))
+    assert np.array_equal(c.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: f"A{c[0]}B{c[1]}")
+def test_gemm_mfma_layout_random_scales(orc, combo):
+    from fp4_microscaling_quantization_amd import mxq
+    m, n, k = 272, 528, 2560
+    (fa, ga), (fb, gb) = combo
+    g = np.random.Generator(np.random.PCG64(11))
+    ac, as_ = _rand_codes(g, m, k, fa, ga, orc, 100, 150)
+    bc, bs = _rand_codes(g, n, k, fb, gb, orc, 100, 150)
+    say("gemm tiled scales", combo)
+    ta, tas = _tiled(orc, ac, as_, fa)
+    tb, tbs = _tiled(orc, bc, bs, fb)
+    c1 = host(mxq.wgrad_gemm(ta, tas, fa, ga, tb, tbs, fb, gb, layout=mxq.LAYOUT_MFMA, m=m, n=n, k=k))
+    c2 = host(mxq.wgrad_gemm(ta, tas, fa, ga, tb, tbs, fb, gb, layout=mxq.LAYOUT_MFMA, m=m, n=n, k=k))
+    assert np.array_equal(c1, c2)                          # repeatable bit for bit
+    ref = orc.gemm_abt_f64(orc.dequantize(ac, as_, ga, fa), orc.dequantize(bc, bs, gb, fb))
+    err = np.linalg.norm(c1 - ref) / np.linalg.norm(ref)
+    assert err <= 1e-6, err
+
+
+@pytest.mark.parametrize("fmt,grid", [(0, 0), (1, 1)])
+def test_dequantize_mfma_layout(orc, fmt, grid):
+    from fp4_microscaling_quantization_amd import mxq
+    g = np.random.Generator(np.random.PCG64(3 + fmt))
+    lines, k = 40, 640
+    codes, scales = _rand_codes(g, lines, k, fmt, grid, orc, 100, 150)
+    tc, ts = _tiled(orc, codes, scales, fmt)
+    say("dequant tiled", fmt, grid)
+    got = host(mxq.dequantize(tc, ts, fmt, grid, mxq.OUT_F32, layout=mxq.LAYOUT_MFMA,
+                              lines=lines, k=k)).astype(np.float64)
+    assert np.array_equal(got, orc.dequantize(codes, scales, grid, fmt))
+
+
+@pytest.mark.parametrize("variant", ["e1m2_e2m3", "e2m1_fp4"])
+def test_wgrad_step_full_size_mfma_layout(orc, variant):
+    """The benchmark's configuration: dY, X 8192 x 4096 quantized column-wise
+    straight into the matrix-core layout, then dW = dY^T X; 96 x 96 sampled
+    outputs against the oracle pipeline."""
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    dy = synth.dy_8192x4096()
+    xx = synth.x_wgrad_8192x4096()
+    signs = synth.sign_mask(synth.SIGNS_WGRAD, 16)
+    grid, fmt = (1, 1) if variant == "e1m2_e2m3" else (0, 0)
+    kd = dict(grid=grid, round=1, hadamard_n=16, sign_mask=signs, sr_seed=synth.SR_SEED_WGRAD)
+    kx = dict(grid=grid, round=0, hadamard_n=16, sign_mask=signs)
+    say("wgrad full tiled", variant)
+    qd = mxq.quantize(to_dev_bf16(dy), row=False, col=True, col_fmt=fmt,
+                      col_layout=mxq.LAYOUT_MFMA, **kd)["col"]
+    qx = mxq.quantize(to_dev_bf16(xx), row=False, col=True, col_fmt=fmt,
+                      col_layout=mxq.LAYOUT_MFMA, **kx)["col"]
+    c = mxq.wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid,
+                       layout=mxq.LAYOUT_MFMA, m=4096, n=4096, k=8192)
+    torch.cuda.synchronize()
+    g = np.random.Generator(np.random.PCG64(23))
+    I = np.sort(g.choice(4096, 96, replace=False))
+    J = np.sort(g.choice(4096, 96, replace=False))
+    pd, px = orc.qparams(**kd), orc.qparams(**kx)
+    A = np.concatenate([orc.dequantize(*orc.quantize_lines(dy, orc.AXIS_COL, pd, int(i), 1, fmt), grid, fmt) for i in I])
+    B = np.concatenate([orc.dequantize(*orc.quantize_lines(xx, orc.AXIS_COL, px, int(j), 1, fmt), grid, fmt) for j in J])
+    ref = orc.gemm_abt_f64(A, B)
+    got = c[torch.from_numpy(I).to(c.device)][:, torch.from_numpy(J).to(c.device)].cpu().numpy()
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err <= 1e-6, err

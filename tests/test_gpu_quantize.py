@@ -141,3 +141,29 @@ def test_full_size_workloads_sampled(orc, case):
             c, s = orc.quantize_lines(x, axis, p, l0, 8, case.fmt)
             assert np.array_equal(gs[l0:l0 + 8], s), (key, l0)
             assert np.array_equal(gc[l0:l0 + 8], c), (key, l0)
+
+
+@pytest.mark.parametrize("shape,row,col", [((96, 256), True, False), ((256, 100), False, True),
+                                           ((128, 384), True, True), ((40, 128), True, False),
+                                           ((640, 72), False, True)])
+@pytest.mark.parametrize("knobs", [(0, 0, 16), (1, 1, 32), (1, 0, 0)], ids=_knob_id)
+def test_mfma_layout_outputs(orc, shape, row, col, knobs):
+    """Outputs in the matrix-core operand layout equal the oracle's row-layout
+    output permuted by the oracle's definition of that layout; bytes outside
+    the layout's data (padding lines, absent steps) stay untouched."""
+    from fp4_microscaling_quantization_amd import mxq
+    rows, cols = shape
+    x = synth.normal_outlier_channels(rows, cols, seed=rows, ch_seed=cols, frac=0.03)
+    kw = _params(orc, *knobs, seed=4)
+    say("mfma layout", shape, row, col, knobs)
+    for fmt in (0, 1):
+        q = mxq.quantize(to_dev_bf16(x), row=row, col=col, row_fmt=fmt, col_fmt=fmt,
+                         row_layout=mxq.LAYOUT_MFMA, col_layout=mxq.LAYOUT_MFMA, fill=0xA5, **kw)
+        p = orc.qparams(**kw)
+        for axis, key, on in ((orc.AXIS_ROW, "row", row), (orc.AXIS_COL, "col", col)):
+            if not on:
+                continue
+            c, s = orc.quantize(x, axis, p, fmt)
+            tc, ts = orc.to_mfma_layout(c, s, fmt, fill=0xA5)
+            assert np.array_equal(host(q[key][1]), ts), (key, "scales")
+            assert np.array_equal(host(q[key][0]), tc), (key, "codes")
