@@ -353,24 +353,6 @@ __device__ __forceinline__ v8i tiled_fragment(const uint8_t *__restrict__ lds, i
     return r;
 }
 
-// Copy this wave's share of one operand's step (16 tiles x 64 x BB bytes,
-// i.e. BB chunks of 1 KB) into LDS.  Tiles past the operand's last tile are
-// clamped to it (their rows are never stored).
-template <int F>
-__device__ __forceinline__ void tiled_stage(const uint8_t *__restrict__ codes, int64_t ntiles,
-                                            int64_t t0, int64_t s, uint8_t *lds, int chunk0,
-                                            int nchunks, int lane)
-{
-    constexpr int BB = blk_bytes<F>(), TB = 64 * BB;
-    const uint8_t *stepbase = codes + s * ntiles * TB;
-    for (int i = 0; i < nchunks; ++i) {
-        const int ch = chunk0 + i;
-        const int o = ch * 1024 + lane * 16;          // byte within the 16-tile run
-        const int64_t tile = min(t0 + o / TB, ntiles - 1);
-        dma16(stepbase + tile * TB + (o % TB), lds + ch * 1024);
-    }
-}
-
 template <int FA, int FB>
 constexpr int tiled_lds_bytes() { return 2 * 16 * 64 * (blk_bytes<FA>() + blk_bytes<FB>()); }
 
@@ -396,30 +378,42 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_tiled(const uint8_t *_
     const int64_t ntA = (m + 15) / 16, ntB = (n + 15) / 16;
     const int64_t nsteps = k / 128;
 
-    // this wave's chunks: a contiguous run over [A chunks | B chunks]
-    const int c0 = wv * PER;
+    // This wave's chunks: a contiguous run over [A chunks | B chunks].  Each
+    // lane's source offset inside a step and its LDS slot are the same for
+    // every step, so they are computed once; a step only adds its stride.
+    constexpr int TBA = 64 * blk_bytes<FA>(), TBB = 64 * blk_bytes<FB>();
+    uint32_t goff[PER];      // byte offset inside the operand's step
+    bool isA[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int ch = wv * PER + i;
+        isA[i] = ch < CA;
+        const int cc = isA[i] ? ch : ch - CA;
+        const int tb = isA[i] ? TBA : TBB;
+        const int o = cc * 1024 + lane * 16;
+        // clamp tiles past the operand's last one (their rows are never stored)
+        const int64_t tile = isA[i] ? min(m0 / 16 + o / TBA, ntA - 1) : min(n0 / 16 + o / TBB, ntB - 1);
+        goff[i] = (uint32_t)(tile * tb + o % tb);
+    }
     auto stage = [&](int64_t s, uint8_t *buf) {
-        const int a_lo = c0, a_hi = min(c0 + PER, CA);
-        if (a_hi > a_lo)
-            tiled_stage<FA>(ac, ntA, m0 / 16, s, buf, a_lo, a_hi - a_lo, lane);
-        const int b_lo = max(c0, CA) - CA, b_hi = c0 + PER - CA;
-        if (b_hi > b_lo)
-            tiled_stage<FB>(bc, ntB, n0 / 16, s, buf + SA, b_lo, b_hi - b_lo, lane);
+        const uint8_t *sa_ = ac + s * ntA * TBA, *sb_ = bc + s * ntB * TBB;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ch = wv * PER + i;
+            dma16((isA[i] ? sa_ : sb_) + goff[i], buf + (isA[i] ? ch * 1024 : SA + (ch - CA) * 1024));
+        }
     };
     const uint32_t *sA = reinterpret_cast<const uint32_t *>(as);
     const uint32_t *sB = reinterpret_cast<const uint32_t *>(bs);
+    const int64_t ta0 = m0 / 16 + 8 * wm, tb0 = n0 / 16 + 4 * wn;
     uint32_t ca[8], cb[4], na[8], nb[4];
     auto scales = [&](int64_t q, uint32_t (&xa)[8], uint32_t (&xb)[4]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int64_t tile = min(m0 / 16 + 8 * wm + i, ntA - 1);
-            xa[i] = sA[(q * ntA + tile) * 64 + lane];
-        }
+        for (int i = 0; i < 8; ++i)
+            xa[i] = sA[(q * ntA + min(ta0 + i, ntA - 1)) * 64 + lane];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t tile = min(n0 / 16 + 4 * wn + j, ntB - 1);
-            xb[j] = sB[(q * ntB + tile) * 64 + lane];
-        }
+        for (int j = 0; j < 4; ++j)
+            xb[j] = sB[(q * ntB + min(tb0 + j, ntB - 1)) * 64 + lane];
     };
 
     v4f acc[8][4];
