@@ -19,6 +19,7 @@
 // "Eficiencia": the fused rotate + quantize).
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
+#include "quant_out.hpp"
 
 namespace mxq {
 
@@ -44,33 +45,6 @@ __device__ __forceinline__ uint4 load8_scalar(const uint16_t *__restrict__ p)
         h[j] = p[j];
     return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                       h[6] | (h[7] << 16));
-}
-
-// Where an output's blocks go (MXQ_LAYOUT_ROWS or MXQ_LAYOUT_MFMA).
-struct OutDesc {
-    uint8_t *codes;
-    uint8_t *scales;
-    int fmt;
-    int layout;
-    uint64_t nbk;     // blocks per line
-    uint64_t ntiles;  // 16-line tiles (MFMA layout)
-};
-
-__device__ __forceinline__ uint64_t code_offset(const OutDesc &o, uint64_t line, uint64_t jb, int bb)
-{
-    if (o.layout == MXQ_LAYOUT_ROWS)
-        return (line * o.nbk + jb) * bb;
-    // [step = jb / 4][tile = line / 16][lane = 16 (jb % 4) + line % 16]
-    return (((jb >> 2) * o.ntiles + (line >> 4)) * 64 + 16 * (jb & 3) + (line & 15)) * bb;
-}
-
-__device__ __forceinline__ uint64_t scale_offset(const OutDesc &o, uint64_t line, uint64_t jb)
-{
-    if (o.layout == MXQ_LAYOUT_ROWS)
-        return line * o.nbk + jb;
-    // [group = jb / 16][tile][lane] words, byte = step within the group
-    return (((jb >> 4) * o.ntiles + (line >> 4)) * 64 + 16 * (jb & 3) + (line & 15)) * 4 +
-           ((jb >> 2) & 3);
 }
 
 // Store this lane's slice of block (line, jb): FP4 4 bytes at 4*pos, or E2M3
@@ -376,7 +350,11 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
     q.s = static_cast<hipStream_t>(stream);
 
     hipError_t e;
-    if (cfg->grid == MXQ_GRID_E2M1)
+    if (!row_out) {
+        ColLaunch c{q.x, rows, cols, ld_x, q.cout,
+                    (reinterpret_cast<uintptr_t>(x) % 8 == 0 && ld_x % 4 == 0) ? 1 : 0, q.kn, q.s};
+        e = launch_quant_col(cfg->grid, cfg->round, cfg->hadamard_n, c);
+    } else if (cfg->grid == MXQ_GRID_E2M1)
         e = cfg->round == MXQ_ROUND_RTNE ? launch_quant_hn<kE2M1, kRTNE>(cfg->hadamard_n, q)
                                          : launch_quant_hn<kE2M1, kSR>(cfg->hadamard_n, q);
     else

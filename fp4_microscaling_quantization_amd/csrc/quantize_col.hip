@@ -1,0 +1,384 @@
+// Column-wise fused rotate + quantize: blocks of 32 consecutive rows of one
+// column, the kernel behind mxq_quantize when only the column-wise output is
+// requested (the operands of the weight-gradient product dY^T X are both
+// quantized along the token dimension, which is the row dimension of dY and X).
+//
+// Work layout.  A wave covers 32 rows x 128 columns, a workgroup 4 waves
+// stacked along the rows (128 x 128).  Lane (cg, pos) = (lane >> 1, lane & 1)
+// loads rows 16 pos .. 16 pos + 15 of its row band in the four columns
+// 4 cg .. 4 cg + 3 (sixteen 8-byte loads), so it holds 16 consecutive block
+// positions of four column blocks.  The size-16 rotation then runs entirely
+// inside the lane; the two lanes of a block meet (by DPP) only for the block
+// maximum and, for H32, the last butterfly stage.
+//
+// Arithmetic.  The same fp32 operations as the oracle up to exact rewrites:
+//  * The 1/4 normalisation of H16 is folded into the power-of-two scale
+//    multiplier (exact while the rotated value is a normal fp32 number, i.e.
+//    for every block whose scale code is at least 40; lower blocks take the
+//    unfused order).  The block maximum is taken on the unnormalised values
+//    and divided by 4 once (monotone rounding).
+//  * Rounding produces the chosen level as an fp32 value: RTNE by rint after
+//    clamping, SR by ceil(x - (2r + 1) 2^-(B+1)), which rounds up exactly
+//    when the fraction of x above its lower level exceeds (2r + 1) 2^-(B+1).
+//  * The gfx950 scaled converts turn those grid values into FP4 or E2M3 codes
+//    (a value on the grid converts exactly; the scale operand divides by a
+//    power of two).
+//
+// Method sources (web pages): MX blocks of 32 sharing one E8M0 exponent taken
+// from the block's largest magnitude -- htx.com news on "Pretraining large
+// language models with MXFP4", section "Que es MXFP4?"; H16 / H32 rotations
+// and the random sign flips -- gist.science summary "Pre-treinamento de
+// Modelos de Linguagem Grandes com MXFP4", section "Metodologia", and the
+// htx.com news, section "Experimento de diagnostico"; RTNE onto E2M1 or the
+// uniform E1M2 grid and SR on the gradient -- gist.science summary
+// "Repensando o Vies de Encolhimento (Shrinkage Bias) no Pre-treinamento de
+// LLMs em FP4", sections "Metodologia 1" and "Metodologia 2".
+#include "mxq_device.hpp"
+#include "mxq_host.hpp"
+#include "quant_out.hpp"
+
+namespace mxq {
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+// E2M3 codes of 32 fp32 values lying on the E2M3 grid after division by
+// `scale`.  Code k of the 192-bit little-endian result (bits 6k .. 6k+5) is
+// that of a[k / 2] for even k and of b[k / 2] for odd k.  The convert still
+// reads its sources while it writes its destination, so the two must not
+// share registers: the empty asm statement keeps both sources live past the
+// convert, which keeps the register allocator from placing the result on top
+// of them.
+__device__ __forceinline__ void cvt_e2m3_32(const f16v &a, const f16v &b, float scale,
+                                            uint32_t (&out)[6])
+{
+    const auto r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(a, b, scale);
+    asm volatile("" ::"v"(a), "v"(b));
+#pragma unroll
+    for (int i = 0; i < 6; ++i)
+        out[i] = r[i];
+}
+
+// Random values of the lane's 16 positions 16 pos + i as fp32 integers:
+// element j = 16 pos + i of block `blk` takes the counter-based draw of the
+// oracle (Philox4x32-10 on counter (j >> 3 | j >> 4, blk lo, blk hi, stream),
+// half / byte of word (j >> 1) & 3 | (j >> 2) & 3).
+__device__ __forceinline__ void sr_rand16(const QKnobs &kn, int pos, uint64_t blk, float (&rf)[16])
+{
+    const uint32_t blo = (uint32_t)blk, bhi = (uint32_t)(blk >> 32);
+    if (kn.sr_bits == 16) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const Rand4 q = philox4x32_10((uint32_t)(2 * pos + half), blo, bhi, kn.stream,
+                                          kn.seed_lo, kn.seed_hi);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                rf[8 * half + i] = (float)((q.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+        }
+    } else {
+        const Rand4 q = philox4x32_10((uint32_t)pos, blo, bhi, kn.stream, kn.seed_lo, kn.seed_hi);
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            rf[i] = (float)((q.w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
+    }
+}
+
+// The convert scale that maps the values col16 leaves behind onto the grid.
+template <int GRID, int ROUND>
+constexpr float level_unit()
+{
+    return (GRID == kE2M1 && ROUND == kSR) ? 4.0f : 2.0f;
+}
+
+// One column block seen by one lane: v holds positions 16 pos .. 16 pos + 15
+// (bf16 widened, random signs applied).  Rotates, finds the block's E8M0
+// code (returned) and leaves in v the rounded levels times level_unit(), with
+// the sign of the rotated value (for E2M1 with RTNE and FP4 output, the
+// unrounded value times 2: the FP4 convert rounds it).
+template <int GRID, int ROUND, int HN, bool EXACT_LEVEL>
+__device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk, const QKnobs &kn,
+                                          float h, float h2)
+{
+    constexpr int EMAX = GRID == kE2M1 ? 2 : 1;
+    // ---- rotation: fp32 butterflies of stride 1, 2, 4, 8 in the lane, 16 across
+    if constexpr (HN >= 16) {
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (!(i & s)) {
+                    const float p = v[i], q = v[i + s];
+                    v[i] = p + q;
+                    v[i + s] = p - q;
+                }
+            }
+        }
+        if constexpr (HN == 32) {
+            // the lower lane keeps u + u', the upper one u - u' (u lower, u' upper)
+            const float beta = pos ? -1.0f : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = __builtin_fmaf(v[i], beta, lane_xor_f<1>(v[i]));
+            const float c = as_f(0x3E3504F3u);  // fl32(1/sqrt(32))
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = v[i] * c;
+        }
+    }
+    // ---- block maximum of |y|
+    uint32_t am;
+    if constexpr (HN >= 16) {
+        // Each output of a rotated sub-block mixes all its inputs: a NaN or Inf
+        // input leaves no finite value in the lane, so fmax (which skips a NaN
+        // operand) still returns a non-finite maximum for such a block.
+        float m = fabsf(v[0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i)
+            m = fmaxf(m, fabsf(v[i]));
+        am = as_u(m);
+    } else {
+        // magnitude maximum on the bit patterns (NaN > Inf > finite): the
+        // signed maximum finds the largest positive value, the unsigned one the
+        // largest negative value
+        uint32_t um = 0;
+        int32_t sm = (int32_t)0x80000000u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            um = max(um, as_u(v[i]));
+            sm = max(sm, (int32_t)as_u(v[i]));
+        }
+        am = max(um & 0x7FFFFFFFu, (uint32_t)sm & 0x7FFFFFFFu);
+    }
+    am = max(am, lane_xor<1>(am));
+    if constexpr (HN == 16)
+        am = as_u(as_f(am) * 0.25f);  // fl(max|v| / 4) = max |fl(v / 4)|
+    const uint32_t sc = am >= 0x7F800000u ? 0xFFu : (uint32_t)max((int)(am >> 23) - EMAX, 0);
+
+    // ---- multiplier m2 = 2 * 2^-e (times 1/4 for H16): v * m2 = 2 y 2^-e
+    float m2;
+    if (sc < 40u) {
+        // low scale: the unfused order (y = v / 4 may be subnormal; 2^-e up to 2^127)
+        const float inv = as_f((254u - sc) << 23);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (HN == 16)
+                v[i] = v[i] * 0.25f;
+            v[i] = v[i] * inv;
+        }
+        m2 = 2.0f;
+    } else {
+        m2 = as_f((255u - min(sc, 253u)) << 23);
+        if constexpr (HN == 16)
+            m2 *= 0.25f;
+    }
+
+    // ---- rounding
+    if constexpr (ROUND == kRTNE) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float t = v[i] * m2;  // 2 a, signed
+            if constexpr (GRID == kE1M2) {
+                // levels 0.5 m: m = RNE(2a), saturated at 7
+                v[i] = rintf(__builtin_amdgcn_fmed3f(t, -7.0f, 7.0f));
+            } else if constexpr (!EXACT_LEVEL) {
+                v[i] = t;  // the FP4 convert rounds t / 2 to nearest even, saturating at 6
+            } else {
+                // E2M1 in software: round 2a to a multiple of 2 step by adding and
+                // subtracting 1.5 2^22 S (S = 2^max(floor(log2 2a), 1), whose ulp is 2 step)
+                const float a2 = fminf(fabsf(t), 12.0f);
+                const float S = as_f(max(as_u(a2) & 0x7F800000u, 0x40000000u));
+                const float G = S * 6291456.0f;
+                v[i] = copysignf((a2 + G) - G, t);
+            }
+        }
+    } else {
+        float rf[16];
+        sr_rand16(kn, pos, blk, rf);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if constexpr (GRID == kE1M2) {
+                // x = min(2a, 7) - h; level index ceil(x - 2 h r)
+                const float x = fminf(__builtin_fmaf(fabsf(v[i]), m2, -h), 7.0f - h);
+                v[i] = copysignf(ceilf(__builtin_fmaf(rf[i], -h2, x)), v[i]);
+            } else {
+                // a in units of the local step (S / 4 for 2a below 2 S): x = 2a * 2 / S
+                const float a2 = fminf(fabsf(v[i]) * m2, 12.0f);
+                const float S = as_f(max(as_u(a2) & 0x7F800000u, 0x40000000u));
+                const float x = __builtin_fmaf(a2, as_f(0x7F800000u - as_u(S)), -h);
+                v[i] = copysignf(ceilf(__builtin_fmaf(rf[i], -h2, x)) * S, v[i]);
+            }
+        }
+    }
+    return sc;
+}
+
+// FP4 nibbles of the 16 values col16 left in v (element i at bits 4i of w).
+template <int GRID, int ROUND>
+__device__ __forceinline__ void pack_fp4(const float (&v)[16], uint32_t sc, uint32_t (&w)[2])
+{
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        uint32_t x = 0;
+        if constexpr (GRID == kE2M1) {
+            constexpr float u = level_unit<GRID, ROUND>();
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 0], v[8 * d + 1], u, 0);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 2], v[8 * d + 3], u, 1);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 4], v[8 * d + 5], u, 2);
+            x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 6], v[8 * d + 7], u, 3);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float q = v[8 * d + i];  // the level index m, signed
+                x |= ((uint32_t)fabsf(q) | ((as_u(q) >> 28) & 8u)) << (4 * i);
+            }
+        }
+        w[d] = sc == 0xFFu ? 0u : x;
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void store_words(const OutDesc &o, uint64_t line, uint64_t jb, int pos,
+                                            const uint32_t *w)
+{
+    uint32_t *d = reinterpret_cast<uint32_t *>(o.codes + code_offset(o, line, jb, 8 * N) +
+                                               4 * N * pos);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        d[k] = w[k];
+}
+
+template <int GRID, int ROUND, int HN, int FMT>
+__global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ x, int64_t rows,
+                                                   int64_t cols, int64_t ld, OutDesc out, int vec,
+                                                   QKnobs kn)
+{
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int pos = lane & 1, cg = lane >> 1;
+    const int64_t rband = (int64_t)blockIdx.y * 128 + wv * 32;  // rows % 32 == 0
+    if (rband >= rows)
+        return;                                                   // whole wave
+    const int64_t r0 = rband + 16 * pos;
+    const int64_t c0 = (int64_t)blockIdx.x * 128 + 4 * cg;
+    const uint64_t jb = (uint64_t)rband >> 5, nbc = (uint64_t)rows >> 5;
+
+    // lo[i]: columns c0, c0 + 1 of row r0 + i; hi[i]: columns c0 + 2, c0 + 3
+    uint32_t lo[16], hi[16];
+    if (vec && c0 + 4 <= cols) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint2 w = *reinterpret_cast<const uint2 *>(x + (r0 + i) * ld + c0);
+            lo[i] = w.x;
+            hi[i] = w.y;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t hh[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                hh[j] = (c0 + j < cols) ? (uint32_t)x[(r0 + i) * ld + c0 + j] : 0u;
+            lo[i] = hh[0] | (hh[1] << 16);
+            hi[i] = hh[2] | (hh[3] << 16);
+        }
+    }
+    // random sign flips: position p = 16 pos + i takes bit p % HN of the mask
+    if constexpr (HN > 0) {
+        const uint32_t sg = HN == 16 ? kn.sign_mask : kn.sign_mask >> (16 * pos);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t f = ((sg >> i) & 1u) ? 0x80008000u : 0u;
+            lo[i] ^= f;
+            hi[i] ^= f;
+        }
+    }
+    const float h = kn.sr_bits == 16 ? 0x1p-17f : 0x1p-9f;  // 2^-(B+1)
+    const float h2 = 2.0f * h;
+    constexpr bool kExact = FMT == MXQ_FMT_E2M3;
+
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+        float a[16], b[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t w = jp ? hi[i] : lo[i];
+            a[i] = as_f(w << 16);
+            b[i] = as_f(w & 0xFFFF0000u);
+        }
+        const int64_t ca = c0 + 2 * jp, cb = ca + 1;
+        const uint32_t sa =
+            col16<GRID, ROUND, HN, kExact>(a, pos, (uint64_t)ca * nbc + jb, kn, h, h2);
+        const uint32_t sb =
+            col16<GRID, ROUND, HN, kExact>(b, pos, (uint64_t)cb * nbc + jb, kn, h, h2);
+        if constexpr (FMT == MXQ_FMT_E2M3) {
+            f16v s0, s1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s0[j] = a[2 * j];
+                s1[j] = a[2 * j + 1];
+                s0[8 + j] = b[2 * j];
+                s1[8 + j] = b[2 * j + 1];
+            }
+            uint32_t o[6];
+            cvt_e2m3_32(s0, s1, level_unit<GRID, ROUND>(), o);
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                o[k] = sa == 0xFFu ? 0u : o[k];
+                o[3 + k] = sb == 0xFFu ? 0u : o[3 + k];
+            }
+            if (ca < cols)
+                store_words<3>(out, (uint64_t)ca, jb, pos, o);
+            if (cb < cols)
+                store_words<3>(out, (uint64_t)cb, jb, pos, o + 3);
+        } else {
+            uint32_t wa[2], wb[2];
+            pack_fp4<GRID, ROUND>(a, sa, wa);
+            pack_fp4<GRID, ROUND>(b, sb, wb);
+            if (ca < cols)
+                store_words<2>(out, (uint64_t)ca, jb, pos, wa);
+            if (cb < cols)
+                store_words<2>(out, (uint64_t)cb, jb, pos, wb);
+        }
+        if (pos == 0) {
+            if (ca < cols)
+                out.scales[scale_offset(out, (uint64_t)ca, jb)] = (uint8_t)sa;
+            if (cb < cols)
+                out.scales[scale_offset(out, (uint64_t)cb, jb)] = (uint8_t)sb;
+        }
+    }
+}
+
+namespace {
+
+template <int GRID, int ROUND, int HN>
+void launch_col_fmt(const ColLaunch &q)
+{
+    const dim3 grid((unsigned)((q.cols + 127) / 128), (unsigned)((q.rows + 127) / 128));
+    if (q.out.fmt == MXQ_FMT_E2M3)
+        hipLaunchKernelGGL((k_quant_col<GRID, ROUND, HN, MXQ_FMT_E2M3>), grid, dim3(256), 0, q.s,
+                           q.x, q.rows, q.cols, q.ld, q.out, q.vec, q.kn);
+    else
+        hipLaunchKernelGGL((k_quant_col<GRID, ROUND, HN, MXQ_FMT_FP4>), grid, dim3(256), 0, q.s,
+                           q.x, q.rows, q.cols, q.ld, q.out, q.vec, q.kn);
+}
+
+template <int GRID, int ROUND>
+void launch_col_hn(int hn, const ColLaunch &q)
+{
+    switch (hn) {
+    case 0: launch_col_fmt<GRID, ROUND, 0>(q); break;
+    case 16: launch_col_fmt<GRID, ROUND, 16>(q); break;
+    default: launch_col_fmt<GRID, ROUND, 32>(q); break;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_col(int grid, int round, int hn, const ColLaunch &q)
+{
+    if (grid == kE2M1)
+        round == kRTNE ? launch_col_hn<kE2M1, kRTNE>(hn, q) : launch_col_hn<kE2M1, kSR>(hn, q);
+    else
+        round == kRTNE ? launch_col_hn<kE1M2, kRTNE>(hn, q) : launch_col_hn<kE1M2, kSR>(hn, q);
+    return hipGetLastError();
+}
+
+}  // namespace mxq
