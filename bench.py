@@ -12,8 +12,13 @@ Inputs are synthetic (seeded numpy), resident in HBM before timing.  Four
 input/output sets rotate so consecutive steps do not hit in the 256 MB
 last-level cache.
 
+Timing: W untimed warmup steps; then the timed region, K whole steps back to
+back between two HIP events (ms_per_step); then each kernel K times back to
+back between two events, which gives its average launch duration without
+event records between launches.
+
 The JSON line reports the fused quantize bandwidth as `value` (algorithmic
-bytes of the two quantize launches / their event-timed duration), the GEMM
+bytes of the two quantize launches / their average durations), the GEMM
 rate under `gemm`, the roofline of the dominant kernel and of each kernel,
 and the CPU oracle timed on a bounded sample as `cpu_baseline`.
 """
@@ -35,6 +40,58 @@ T, N, K = 8192, 4096, 4096     # tokens, out features (dY cols), in features (X 
 def quant_bytes_per_elem(fmt: int) -> float:
     # read bf16 (2 B) + write codes (0.5 B FP4 / 0.75 B E2M3) + 1 scale byte per 32
     return 2.0 + (0.5 if fmt == 0 else 0.75) + 1.0 / 32
+
+
+class HipEvent:
+    """A HIP event created with hipEventDisableSystemFence: recording it takes a
+    timestamp without the system-scope cache writeback / invalidate of a default
+    event, so back-to-back kernels are timed without gaps of the event's own
+    making.  Recorded on the stream the kernels are launched on."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes as C
+        if HipEvent._hip is None:
+            import torch  # noqa: F401  (loads the HIP runtime torch was built with)
+            h = C.CDLL(HipEvent._loaded_runtime())
+            h.hipEventCreateWithFlags.argtypes = [C.POINTER(C.c_void_p), C.c_uint]
+            h.hipEventRecord.argtypes = [C.c_void_p, C.c_void_p]
+            h.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
+            h.hipEventDestroy.argtypes = [C.c_void_p]
+            HipEvent._hip = h
+        self._C = C
+        self.ev = C.c_void_p()
+        st = HipEvent._hip.hipEventCreateWithFlags(C.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+
+    @staticmethod
+    def _loaded_runtime() -> str:
+        # the HIP runtime already mapped into this process (the one torch and
+        # libmxq use): opening it again by path returns the same instance
+        with open("/proc/self/maps") as f:
+            for line in f:
+                path = line.split()[-1]
+                if os.path.basename(path).startswith("libamdhip64.so"):
+                    return path
+        raise RuntimeError("no HIP runtime loaded in this process")
+
+    def record(self, stream):
+        st = HipEvent._hip.hipEventRecord(self.ev, self._C.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed ({st})")
+
+    def elapsed_ms(self, end) -> float:
+        ms = self._C.c_float()
+        st = HipEvent._hip.hipEventElapsedTime(self._C.byref(ms), self.ev, end.ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st})")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
 
 
 def parse():
@@ -96,52 +153,65 @@ def main():
         sets.append((dy, xx, qd, qx, c))
     torch.cuda.synchronize()
 
-    def step(i, ev=None):
-        dy, xx, qd, qx, c = sets[i % len(sets)]
-        if ev is not None:
-            ev[0].record()
-        mxq.quantize_into(cfg_dy, dy, col=(qd[0], qd[1], fmt, mxq.LAYOUT_MFMA))
-        if ev is not None:
-            ev[1].record()
-        mxq.quantize_into(cfg_x, xx, col=(qx[0], qx[1], fmt, mxq.LAYOUT_MFMA))
-        if ev is not None:
-            ev[2].record()
-        mxq.wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, out=c,
-                       layout=mxq.LAYOUT_MFMA, m=N, n=K, k=T)
-        if ev is not None:
-            ev[3].record()
+    # the three launches of each set, marshalled once so that the host stays
+    # ahead of the GPU and the events time the kernels, not the launch path
+    calls = []
+    for dy, xx, qd, qx, c in sets:
+        calls.append((
+            mxq.prepare_quantize(cfg_dy, dy, col=(qd[0], qd[1], fmt, mxq.LAYOUT_MFMA)),
+            mxq.prepare_quantize(cfg_x, xx, col=(qx[0], qx[1], fmt, mxq.LAYOUT_MFMA)),
+            mxq.prepare_wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, c,
+                                   mxq.LAYOUT_MFMA, N, K, T)))
+
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        q_dy, q_x, gemm = calls[i % len(calls)]
+        q_dy()
+        q_x()
+        gemm()
+
+    def timed(fn, n):
+        """GPU time of n calls of fn(i), bracketed by two events (seconds)."""
+        e0, e1 = HipEvent(), HipEvent()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) * 1e-3
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # the timed region: K whole steps back to back
     w0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
+    t_steps = timed(step, args.steps)
     wall = time.perf_counter() - w0
+    # each kernel's average launch duration: K launches of it back to back over
+    # the same rotating sets (no event between launches)
+    t_qdy = timed(lambda i: calls[i % len(calls)][0](), args.steps) / args.steps
+    t_qx = timed(lambda i: calls[i % len(calls)][1](), args.steps) / args.steps
+    t_gm = timed(lambda i: calls[i % len(calls)][2](), args.steps) / args.steps
 
-    q_dy = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3     # seconds
-    q_x = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    gm = np.array([e[2].elapsed_time(e[3]) for e in evs]) * 1e-3
     elems = T * N
     qbytes = elems * quant_bytes_per_elem(fmt)                           # per launch
     flops = 2.0 * N * K * T
-    q_gbs = 2 * qbytes * args.steps / (q_dy.sum() + q_x.sum()) / 1e9
-    g_tflops = flops * args.steps / gm.sum() / 1e12
+    q_gbs = 2 * qbytes / (t_qdy + t_qx) / 1e9
+    g_tflops = flops / t_gm / 1e12
     mfma_peak = MFMA_PEAK_TFLOPS["fp6" if fmt == mxq.FMT_E2M3 else "fp4"]
 
     kernels = {
-        "quantize_dy_col_sr": {"bound": "hbm", "avg_us": q_dy.mean() * 1e6,
-                               "achieved": qbytes / q_dy.mean() / 1e9, "peak": HBM_PEAK_GBS,
+        "quantize_dy_col_sr": {"bound": "hbm", "avg_us": t_qdy * 1e6,
+                               "achieved": qbytes / t_qdy / 1e9, "peak": HBM_PEAK_GBS,
                                "unit": "GB/s"},
-        "quantize_x_col_rtne": {"bound": "hbm", "avg_us": q_x.mean() * 1e6,
-                                "achieved": qbytes / q_x.mean() / 1e9, "peak": HBM_PEAK_GBS,
+        "quantize_x_col_rtne": {"bound": "hbm", "avg_us": t_qx * 1e6,
+                                "achieved": qbytes / t_qx / 1e9, "peak": HBM_PEAK_GBS,
                                 "unit": "GB/s"},
-        "wgrad_gemm": {"bound": "mfma", "avg_us": gm.mean() * 1e6,
-                       "achieved": flops / gm.mean() / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
+        "wgrad_gemm": {"bound": "mfma", "avg_us": t_gm * 1e6,
+                       "achieved": flops / t_gm / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
     }
     for k_ in kernels.values():
         k_["frac"] = k_["achieved"] / k_["peak"]
@@ -160,7 +230,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "ms_per_step": round(t_steps / args.steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -177,6 +247,9 @@ def main():
             "parallelism": "none (1 GPU)",
             "quantize_frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
         },
+        "step": {"gpu_ms": round(t_steps / args.steps * 1e3, 4),
+                 "wall_ms": round(wall / args.steps * 1e3, 4),
+                 "kernels_ms": round((t_qdy + t_qx + t_gm) * 1e3, 4)},
         "gemm": {"value": round(g_tflops, 2), "unit": "TFLOP/s", "peak": mfma_peak,
                  "frac": round(g_tflops / mfma_peak, 4)},
         "roofline": dom,

@@ -246,6 +246,19 @@ __device__ __forceinline__ void store_words(const OutDesc &o, uint64_t line, uin
         d[k] = w[k];
 }
 
+// The same words into the LDS image of a workgroup's MFMA-layout run: column
+// cl (0..127) of the tile, row band wv (0..3, i.e. block 4 by + wv).
+template <int N>
+__device__ __forceinline__ void stage_words(uint32_t *stage, int cl, int wv, int pos,
+                                            const uint32_t *w)
+{
+    const int slot = (cl >> 4) * 64 + 16 * wv + (cl & 15);
+    uint32_t *d = stage + slot * (2 * N) + N * pos;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        d[k] = w[k];
+}
+
 template <int GRID, int ROUND, int HN, int FMT>
 __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ x, int64_t rows,
                                                    int64_t cols, int64_t ld, OutDesc out, int vec,
@@ -254,6 +267,12 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int pos = lane & 1, cg = lane >> 1;
     const int64_t rband = (int64_t)blockIdx.y * 128 + wv * 32;  // rows % 32 == 0
+    // In the MFMA layout (rows % 128 == 0) a full 128-column tile's codes form
+    // one contiguous run: stage them in LDS and write the run with 16-byte
+    // stores.  Every wave of such a workgroup has rows, so none returns early.
+    constexpr int BB = FMT == MXQ_FMT_E2M3 ? 24 : 16;           // bytes per block
+    __shared__ uint32_t stage[128 * BB];                         // 8 tiles x 64 slots
+    const bool staged = out.layout == MXQ_LAYOUT_MFMA && (int64_t)blockIdx.x * 128 + 128 <= cols;
     if (rband >= rows)
         return;                                                   // whole wave
     const int64_t r0 = rband + 16 * pos;
@@ -324,18 +343,28 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
                 o[k] = sa == 0xFFu ? 0u : o[k];
                 o[3 + k] = sb == 0xFFu ? 0u : o[3 + k];
             }
-            if (ca < cols)
-                store_words<3>(out, (uint64_t)ca, jb, pos, o);
-            if (cb < cols)
-                store_words<3>(out, (uint64_t)cb, jb, pos, o + 3);
+            if (staged) {
+                stage_words<3>(stage, 4 * cg + 2 * jp, wv, pos, o);
+                stage_words<3>(stage, 4 * cg + 2 * jp + 1, wv, pos, o + 3);
+            } else {
+                if (ca < cols)
+                    store_words<3>(out, (uint64_t)ca, jb, pos, o);
+                if (cb < cols)
+                    store_words<3>(out, (uint64_t)cb, jb, pos, o + 3);
+            }
         } else {
             uint32_t wa[2], wb[2];
             pack_fp4<GRID, ROUND>(a, sa, wa);
             pack_fp4<GRID, ROUND>(b, sb, wb);
-            if (ca < cols)
-                store_words<2>(out, (uint64_t)ca, jb, pos, wa);
-            if (cb < cols)
-                store_words<2>(out, (uint64_t)cb, jb, pos, wb);
+            if (staged) {
+                stage_words<2>(stage, 4 * cg + 2 * jp, wv, pos, wa);
+                stage_words<2>(stage, 4 * cg + 2 * jp + 1, wv, pos, wb);
+            } else {
+                if (ca < cols)
+                    store_words<2>(out, (uint64_t)ca, jb, pos, wa);
+                if (cb < cols)
+                    store_words<2>(out, (uint64_t)cb, jb, pos, wb);
+            }
         }
         if (pos == 0) {
             if (ca < cols)
@@ -343,6 +372,17 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
             if (cb < cols)
                 out.scales[scale_offset(out, (uint64_t)cb, jb)] = (uint8_t)sb;
         }
+    }
+    if (staged) {
+        // the workgroup's 4 row bands are the 4 lane groups of one k-step: the
+        // 8 tiles x 64 slots of that step start at line 128 bx, block 4 by
+        __syncthreads();
+        uint4 *dst = reinterpret_cast<uint4 *>(
+            out.codes + code_offset(out, (uint64_t)blockIdx.x * 128, (uint64_t)blockIdx.y * 4, BB));
+        const uint4 *src = reinterpret_cast<const uint4 *>(stage);
+#pragma unroll
+        for (int k = 0; k < BB / 8; ++k)
+            dst[k * 256 + t] = src[k * 256 + t];
     }
 }
 

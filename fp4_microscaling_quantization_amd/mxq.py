@@ -164,6 +164,31 @@ def quantize_into(cfg: QConfig, x, row=None, col=None, rows=None, cols=None, ld=
     _check("mxq_quantize", st)
 
 
+def prepare_quantize(cfg: QConfig, x, row=None, col=None, stream=None):
+    """The call quantize_into(cfg, x, row, col) marshalled once: returns a
+    function of no arguments that launches it again on the same buffers (for
+    timing loops, where per-call argument conversion would leave the GPU
+    waiting on the host)."""
+    rows, cols, ld = x.shape[0], x.shape[1], x.stride(0)
+
+    def desc(o):
+        if not o:
+            return None
+        lay = o[3] if len(o) > 3 else LAYOUT_ROWS
+        return QTensor(o[0].data_ptr(), o[1].data_ptr(), o[2], cfg.grid, lay)
+    rt, ct = desc(row), desc(col)
+    cfg_ = QConfig.from_buffer_copy(cfg)
+    args = (C.byref(cfg_), _ptr(x), rows, cols, ld, C.byref(rt) if rt else None,
+            C.byref(ct) if ct else None, _stream(stream))
+    fn = lib().mxq_quantize
+    keep = (cfg_, rt, ct)
+
+    def call():
+        _check("mxq_quantize", fn(*args))
+    call._keep = keep
+    return call
+
+
 def quantize(x, grid=GRID_E2M1, round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
              sr_bits=16, row=True, col=False, row_fmt=FMT_FP4, col_fmt=FMT_FP4,
              row_layout=LAYOUT_ROWS, col_layout=LAYOUT_ROWS, fill=None, stream=None):
@@ -214,6 +239,20 @@ def wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_gri
     _check("mxq_wgrad_gemm", lib().mxq_wgrad_gemm(C.byref(qa), C.byref(qb), m, n, k, _ptr(c),
                                                   c.stride(0), _stream(stream)))
     return c
+
+
+def prepare_wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid, out,
+                       layout, m, n, k, stream=None):
+    """wgrad_gemm(...) marshalled once into a function of no arguments."""
+    qa = qtensor(a_codes, a_scales, a_fmt, a_grid, layout)
+    qb = qtensor(b_codes, b_scales, b_fmt, b_grid, layout)
+    args = (C.byref(qa), C.byref(qb), m, n, k, _ptr(out), out.stride(0), _stream(stream))
+    fn = lib().mxq_wgrad_gemm
+
+    def call():
+        _check("mxq_wgrad_gemm", fn(*args))
+    call._keep = (qa, qb)
+    return call
 
 
 def bias_stats(x, axis: int, codes, scales, fmt: int, grid=GRID_E2M1, round=RTNE, hadamard_n=0,
