@@ -11,7 +11,8 @@
 // inside the lane; the two lanes of a block meet (by DPP) only for the block
 // maximum and, for H32, the last butterfly stage.
 //
-// Arithmetic.  The same fp32 operations as the oracle up to exact rewrites:
+// Arithmetic.  The fp32 operations of the method's definition (fp32 butterfly
+// stages in order, then the scale and the rounding), up to exact rewrites:
 //  * The 1/4 normalisation of H16 is folded into the power-of-two scale
 //    multiplier (exact while the rotated value is a normal fp32 number, i.e.
 //    for every block whose scale code is at least 40; lower blocks take the
@@ -59,9 +60,10 @@ __device__ __forceinline__ void cvt_e2m3_32(const f16v &a, const f16v &b, float 
 }
 
 // Random values of the lane's 16 positions 16 pos + i as fp32 integers:
-// element j = 16 pos + i of block `blk` takes the counter-based draw of the
-// oracle (Philox4x32-10 on counter (j >> 3 | j >> 4, blk lo, blk hi, stream),
-// half / byte of word (j >> 1) & 3 | (j >> 2) & 3).
+// element j = 16 pos + i of block `blk` takes Philox4x32-10 on counter
+// (j >> 3, blk lo, blk hi, stream), half j & 1 of word (j >> 1) & 3 for
+// 16-bit draws; counter (j >> 4, ...), byte j & 3 of word (j >> 2) & 3 for
+// 8-bit draws (the definition in include/mxq.h).
 __device__ __forceinline__ void sr_rand16(const QKnobs &kn, int pos, uint64_t blk, float (&rf)[16])
 {
     const uint32_t blo = (uint32_t)blk, bhi = (uint32_t)(blk >> 32);
