@@ -1,4 +1,4 @@
-// Version and status strings of the libmxq C ABI.
+// Version, status strings and host helpers of the libmxq C ABI.
 #include "mxq.h"
 
 extern "C" const char *mxq_status_string(mxq_status s)
@@ -16,3 +16,32 @@ extern "C" const char *mxq_status_string(mxq_status s)
 }
 
 extern "C" int32_t mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC'11): ten rounds of two 32x32->64-bit products, the high
+// halves xored into the other words with the round key, the key bumped by
+// the two Weyl constants after each round.
+static void philox_host(uint32_t ctr[4], uint32_t k0, uint32_t k1)
+{
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * ctr[0];
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * ctr[2];
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ ctr[1] ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ ctr[3] ^ k1;
+        ctr[1] = (uint32_t)p1;
+        ctr[3] = (uint32_t)p0;
+        ctr[0] = n0;
+        ctr[2] = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+extern "C" uint32_t mxq_rht_sign_mask(uint64_t seed, uint32_t n)
+{
+    if (n != 16 && n != 32)
+        return 0;
+    uint32_t ctr[4] = {0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
+    philox_host(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
+    return n == 32 ? ctr[0] : (ctr[0] & 0xFFFFu);
+}

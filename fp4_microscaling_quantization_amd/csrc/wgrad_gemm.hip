@@ -611,3 +611,9 @@ extern "C" mxq_status mxq_wgrad_gemm(const mxq_qtensor *a, const mxq_qtensor *b,
         hipLaunchKernelGGL((k_wgrad_simple<kMfmaFP6, kMfmaFP4>), grid, dim3(256), 0, s, ac, a->scales, bc, b->scales, m, n, k, c, ldc);
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
 }
+
+extern "C" mxq_status mxq_gemm_abt(const mxq_qtensor *a, const mxq_qtensor *b, int64_t m,
+                                   int64_t n, int64_t k, float *c, int64_t ldc, void *stream)
+{
+    return mxq_wgrad_gemm(a, b, m, n, k, c, ldc, stream);
+}

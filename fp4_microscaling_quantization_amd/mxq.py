@@ -21,9 +21,9 @@ LAYOUT_ROWS, LAYOUT_MFMA = 0, 1
 AXIS_ROW, AXIS_COL = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 
-SYMBOLS = ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_bias_stats",
-           "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_status_string",
-           "mxq_abi_version")
+SYMBOLS = ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "mxq_bias_stats",
+           "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_rht_sign_mask",
+           "mxq_status_string", "mxq_abi_version")
 
 
 class QConfig(C.Structure):
@@ -67,6 +67,9 @@ def lib() -> C.CDLL:
         L.mxq_dequantize.argtypes = [C.POINTER(QTensor), i64, i64, i32, P, i64, P]
         L.mxq_wgrad_gemm.argtypes = [C.POINTER(QTensor), C.POINTER(QTensor), i64, i64, i64, P,
                                      i64, P]
+        L.mxq_gemm_abt.argtypes = L.mxq_wgrad_gemm.argtypes
+        L.mxq_rht_sign_mask.argtypes = [C.c_uint64, C.c_uint32]
+        L.mxq_rht_sign_mask.restype = C.c_uint32
         L.mxq_bias_stats.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, i32, C.POINTER(QTensor),
                                      P, P, C.c_size_t, P]
         L.mxq_bias_stats_workspace_size.argtypes = [i64, i64, i32]
@@ -75,8 +78,8 @@ def lib() -> C.CDLL:
         L.mxq_status_string.argtypes = [i32]
         L.mxq_status_string.restype = C.c_char_p
         L.mxq_abi_version.restype = i32
-        for name in ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_bias_stats",
-                     "mxq_round_to_grid"):
+        for name in ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt",
+                     "mxq_bias_stats", "mxq_round_to_grid"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -253,6 +256,29 @@ def prepare_wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fm
         _check("mxq_wgrad_gemm", fn(*args))
     call._keep = (qa, qb)
     return call
+
+
+def gemm_abt(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid, out=None,
+             layout=LAYOUT_ROWS, m=None, n=None, k=None, stream=None):
+    """C [m x n] fp32 = A [m x k] B [n x k]^T through mxq_gemm_abt: Fprop
+    (X row-wise, W row-wise), Dgrad (dY row-wise, W column-wise) or Wgrad
+    (dY column-wise, X column-wise)."""
+    import torch
+    if layout == LAYOUT_ROWS:
+        m = a_scales.shape[0] if m is None else m
+        n = b_scales.shape[0] if n is None else n
+        k = a_scales.shape[1] * 32 if k is None else k
+    c = torch.empty((m, n), dtype=torch.float32, device=a_codes.device) if out is None else out
+    qa = qtensor(a_codes, a_scales, a_fmt, a_grid, layout)
+    qb = qtensor(b_codes, b_scales, b_fmt, b_grid, layout)
+    _check("mxq_gemm_abt", lib().mxq_gemm_abt(C.byref(qa), C.byref(qb), m, n, k, _ptr(c),
+                                              c.stride(0), _stream(stream)))
+    return c
+
+
+def rht_sign_mask(seed: int, n: int) -> int:
+    """Sign mask of the randomized Hadamard rotation drawn from `seed` (host)."""
+    return int(lib().mxq_rht_sign_mask(seed, n))
 
 
 def bias_stats(x, axis: int, codes, scales, fmt: int, grid=GRID_E2M1, round=RTNE, hadamard_n=0,

@@ -133,6 +133,12 @@ def x_wgrad_8192x4096() -> np.ndarray:
     return x_8192x4096(seed=6, ch_seed=16)
 
 
+def dy_8192x14336() -> np.ndarray:
+    """Upstream gradient of the 14336-wide up-projection output for 8192 tokens
+    (the gradient recipe: Laplace(0,1e-3), 0.1% of entries x100), seeds 8 / 18."""
+    return laplace_outlier_entries(8192, 14336, seed=8, out_seed=18)
+
+
 SIGNS_W = 1002      # 32-bit mask for the weight's H32 RHT
 SIGNS_DY = 1004     # 16-bit mask for the gradient's H16 RHT
 SIGNS_WGRAD = 1005  # 16-bit mask shared by dY and X of the weight-gradient step

@@ -191,6 +191,20 @@ mxq_status mxq_dequantize(const mxq_qtensor *q, int64_t lines, int64_t k, int32_
 mxq_status mxq_wgrad_gemm(const mxq_qtensor *a, const mxq_qtensor *b, int64_t m, int64_t n,
                           int64_t k, float *c, int64_t ldc, void *stream);
 
+/* The same block-scaled product under its general name, for the three GEMMs
+ * of a linear layer in the htx.com news ("Experimento de diagnostico"):
+ *   Fprop  Y [T x N]  = X [T x K] W^T:  a = X row-wise,  b = W row-wise
+ *          (m = T, n = N, k = K);
+ *   Dgrad  dX [T x K] = dY [T x N] W:  a = dY row-wise, b = W column-wise
+ *          (W's blocks run along N; m = T, n = K, k = N);
+ *   Wgrad  dW [N x K] = dY^T X:        a = dY column-wise, b = X column-wise
+ *          (m = N, n = K, k = T).
+ * Both operands of one product must carry the same rotation along k (same
+ * hadamard_n and sign_mask), which then cancels in the product.  Arguments,
+ * requirements and errors as mxq_wgrad_gemm. */
+mxq_status mxq_gemm_abt(const mxq_qtensor *a, const mxq_qtensor *b, int64_t m, int64_t n,
+                        int64_t k, float *c, int64_t ldc, void *stream);
+
 /* Bias / SQNR statistics of the shrinkage-bias summary ("Metodologia 1",
  * "Resultados Experimentais") for a tensor q produced by mxq_quantize from x
  * with the same cfg and axis; the rotated y is recomputed exactly as the
@@ -211,6 +225,15 @@ size_t mxq_bias_stats_workspace_size(int64_t rows, int64_t cols, int32_t axis);
  * rand may be NULL for RTNE.  a, rand, codes are device arrays of n items. */
 mxq_status mxq_round_to_grid(int32_t grid, int32_t round, int32_t sr_bits, const float *a,
                              const uint16_t *rand, int64_t n, uint8_t *codes, void *stream);
+
+/* A random sign mask for the randomized Hadamard rotation (RHT: random sign
+ * inversion before the transform, htx.com news "Experimento de diagnostico";
+ * gist.science summary "Pre-treinamento de Modelos de Linguagem Grandes com
+ * MXFP4", "Metodologia"), drawn from a seed: the low n bits (n = 16 or 32) of
+ * output word 0 of Philox4x32-10 with key (lo32(seed), hi32(seed)) and counter
+ * (0, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF) -- a counter no block of the
+ * stochastic-rounding stream uses.  Host function; returns 0 for other n. */
+uint32_t mxq_rht_sign_mask(uint64_t seed, uint32_t n);
 
 const char *mxq_status_string(mxq_status s);
 int32_t mxq_abi_version(void);

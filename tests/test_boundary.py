@@ -131,3 +131,15 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower() or f == "synth.py", f
+
+
+def test_rht_sign_mask_is_philox_word0(mxq_lib, orc):
+    """mxq_rht_sign_mask (host code of the library) against the oracle's own
+    Philox4x32-10, itself pinned to rocRAND: word 0 of the draw at counter
+    (0, ~0, ~0, ~0) under key (lo, hi) of the seed, low n bits."""
+    for seed in (0, 1, 1002, 1005, 0xDEADBEEFCAFEF00D, (1 << 64) - 1):
+        w = int(orc.philox4x32_10([0, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF],
+                                  [seed & 0xFFFFFFFF, seed >> 32])[0])
+        assert mxq_lib.rht_sign_mask(seed, 32) == w
+        assert mxq_lib.rht_sign_mask(seed, 16) == w & 0xFFFF
+    assert mxq_lib.rht_sign_mask(7, 8) == 0

@@ -1,0 +1,103 @@
+"""The other two GEMMs of a linear layer through mxq_gemm_abt, at the shapes
+of an 8B-model MLP up-projection (8192 tokens, K = 4096, N = 14336), with the
+operands quantized by the GPU straight into the matrix-core layout:
+
+  Fprop  Y  = X W^T : X row-wise, W row-wise (both rotated along K);
+  Dgrad  dX = dY W  : dY row-wise, W column-wise (both rotated along N).
+
+W's two operands come from one dual-output quantize call, which rotates each
+direction with the same knobs.  64 x 64 sampled outputs are checked against
+the oracle's own pipeline (oracle quantize of the sampled lines -> dequantize
+-> fp64 dot products), relative Frobenius error <= 1e-6 (fp32 accumulation of
+MFMA partial sums; the fp64 reference has no rounding of its own at this
+level)."""
+import numpy as np
+import pytest
+
+from fp4_microscaling_quantization_amd import synth
+from gpuhelp import say, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+T, K, N = 8192, 4096, 14336
+VARIANTS = {"e1m2_e2m3": (1, 1), "e2m1_fp4": (0, 0)}   # (grid, fmt)
+
+
+def _sampled_check(orc, c, lines_a, lines_b, I, J):
+    import torch
+    A = np.concatenate(lines_a)
+    B = np.concatenate(lines_b)
+    ref = orc.gemm_abt_f64(A, B)
+    got = c[torch.from_numpy(I).to(c.device)][:, torch.from_numpy(J).to(c.device)].cpu().numpy()
+    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert err <= 1e-6, err
+
+
+@pytest.fixture(scope="module")
+def weight():
+    return synth.w_14336x4096()
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_fprop_full_size_sampled(orc, weight, variant):
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    grid, fmt = VARIANTS[variant]
+    x = synth.x_8192x4096()
+    kn = dict(grid=grid, round=0, hadamard_n=32, sign_mask=synth.sign_mask(synth.SIGNS_W, 32))
+    say("fprop", variant)
+    qx = mxq.quantize(to_dev_bf16(x), row=True, col=False, row_fmt=fmt,
+                      row_layout=mxq.LAYOUT_MFMA, **kn)["row"]
+    qw = mxq.quantize(to_dev_bf16(weight), row=True, col=True, row_fmt=fmt, col_fmt=fmt,
+                      row_layout=mxq.LAYOUT_MFMA, col_layout=mxq.LAYOUT_MFMA, **kn)
+    y = mxq.gemm_abt(qx[0], qx[1], fmt, grid, qw["row"][0], qw["row"][1], fmt, grid,
+                     layout=mxq.LAYOUT_MFMA, m=T, n=N, k=K)
+    torch.cuda.synchronize()
+    g = np.random.Generator(np.random.PCG64(31))
+    I = np.sort(g.choice(T, 64, replace=False))
+    J = np.sort(g.choice(N, 64, replace=False))
+    p = orc.qparams(**kn)
+    la = [orc.dequantize(*orc.quantize_lines(x, orc.AXIS_ROW, p, int(i), 1, fmt), grid, fmt) for i in I]
+    lb = [orc.dequantize(*orc.quantize_lines(weight, orc.AXIS_ROW, p, int(j), 1, fmt), grid, fmt)
+          for j in J]
+    _sampled_check(orc, y, la, lb, I, J)
+
+
+@pytest.mark.parametrize("variant", list(VARIANTS))
+def test_dgrad_full_size_sampled(orc, weight, variant):
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    grid, fmt = VARIANTS[variant]
+    dy = synth.dy_8192x14336()
+    signs = synth.sign_mask(synth.SIGNS_W, 32)
+    kw = dict(grid=grid, round=0, hadamard_n=32, sign_mask=signs)
+    kd = dict(grid=grid, round=1, hadamard_n=32, sign_mask=signs, sr_seed=11)   # SR on the gradient
+    say("dgrad", variant)
+    qd = mxq.quantize(to_dev_bf16(dy), row=True, col=False, row_fmt=fmt,
+                      row_layout=mxq.LAYOUT_MFMA, **kd)["row"]
+    qw = mxq.quantize(to_dev_bf16(weight), row=True, col=True, row_fmt=fmt, col_fmt=fmt,
+                      row_layout=mxq.LAYOUT_MFMA, col_layout=mxq.LAYOUT_MFMA, **kw)
+    dx = mxq.gemm_abt(qd[0], qd[1], fmt, grid, qw["col"][0], qw["col"][1], fmt, grid,
+                      layout=mxq.LAYOUT_MFMA, m=T, n=K, k=N)
+    torch.cuda.synchronize()
+    g = np.random.Generator(np.random.PCG64(37))
+    I = np.sort(g.choice(T, 64, replace=False))
+    J = np.sort(g.choice(K, 64, replace=False))
+    pd, pw = orc.qparams(**kd), orc.qparams(**kw)
+    la = [orc.dequantize(*orc.quantize_lines(dy, orc.AXIS_ROW, pd, int(i), 1, fmt), grid, fmt) for i in I]
+    lb = [orc.dequantize(*orc.quantize_lines(weight, orc.AXIS_COL, pw, int(j), 1, fmt), grid, fmt)
+          for j in J]
+    _sampled_check(orc, dx, la, lb, I, J)
+
+
+def test_gemm_abt_is_the_wgrad_product():
+    """The general entry point and the weight-gradient one are the same call."""
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    x = synth.normal(512, 384, seed=41)
+    q = mxq.quantize(to_dev_bf16(x), grid=1, row=False, col=True, col_fmt=1,
+                     col_layout=mxq.LAYOUT_MFMA)["col"]
+    a = mxq.gemm_abt(q[0], q[1], 1, 1, q[0], q[1], 1, 1, layout=mxq.LAYOUT_MFMA, m=384, n=384, k=512)
+    b = mxq.wgrad_gemm(q[0], q[1], 1, 1, q[0], q[1], 1, 1, layout=mxq.LAYOUT_MFMA, m=384, n=384, k=512)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
