@@ -147,6 +147,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-fusion", action="store_true",
+                    help="skip the fused / standalone / unfused quantize comparison")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -298,6 +300,9 @@ def main():
         "kernels": kernels,
     }
 
+    if not args.no_fusion:
+        rec["fusion"] = fusion_ratios(torch, mxq, synth, dev, max(args.steps, 10))
+
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -312,6 +317,75 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, args.cpu_seconds)
 
     print(json.dumps(rec), flush=True)
+
+
+def fusion_ratios(torch, mxq, synth, dev, reps):
+    """The rotation fused into the quantizer against the plain quantizer (no
+    rotation) and against the unfused pair (a rotation kernel writing bf16,
+    then the plain quantizer reading it back), on the activation workload
+    (X 8192 x 4096, row-wise, H16) and the weight workload (W 14336 x 4096,
+    row- and column-wise outputs, H32 + random signs).  Each variant is timed
+    as `reps` back-to-back launches over two input/output sets."""
+    import numpy as np
+
+    def timed(calls):
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0, e1 = HipEvent(), HipEvent()
+        for c in calls[0]:
+            c()
+        torch.cuda.synchronize()
+        e0.record(s)
+        for i in range(reps):
+            for c in calls[i % len(calls)]:
+                c()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_ms(e1) * 1e3 / reps          # us per repetition
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    out = {}
+    workloads = [
+        ("activation_8192x4096_row_h16", synth.x_8192x4096(), 16, 0, True, False),
+        ("weight_14336x4096_dual_h32", synth.w_14336x4096(), 32,
+         synth.sign_mask(synth.SIGNS_W, 32), True, True),
+    ]
+    for name, x_np, hn, mask, row, col in workloads:
+        rows, cols = x_np.shape
+        sets = []
+        for _ in range(2):
+            x = to_dev(x_np)
+            r = mxq.empty_qtensor(rows, cols, mxq.FMT_FP4, dev) if row else None
+            c = mxq.empty_qtensor(cols, rows, mxq.FMT_FP4, dev) if col else None
+            rot_r = torch.empty_like(x) if row else None
+            rot_c = torch.empty_like(x) if col else None
+            sets.append((x, r, c, rot_r, rot_c))
+        fused, plain, unfused = [], [], []
+        cf = mxq.qconfig(grid=mxq.GRID_E2M1, round=mxq.RTNE, hadamard_n=hn, sign_mask=mask)
+        c0 = mxq.qconfig(grid=mxq.GRID_E2M1, round=mxq.RTNE)
+        for x, r, c, rot_r, rot_c in sets:
+            ro = (r[0], r[1], mxq.FMT_FP4) if row else None
+            co = (c[0], c[1], mxq.FMT_FP4) if col else None
+            fused.append([mxq.prepare_quantize(cf, x, row=ro, col=co)])
+            plain.append([mxq.prepare_quantize(c0, x, row=ro, col=co)])
+            u = []
+            if row:
+                u.append(mxq.prepare_rotate(x, mxq.AXIS_ROW, hn, mask, mxq.OUT_BF16, rot_r))
+                u.append(mxq.prepare_quantize(c0, rot_r, row=ro))
+            if col:
+                u.append(mxq.prepare_rotate(x, mxq.AXIS_COL, hn, mask, mxq.OUT_BF16, rot_c))
+                u.append(mxq.prepare_quantize(c0, rot_c, col=co))
+            unfused.append(u)
+        tf, tp, tu = timed(fused), timed(plain), timed(unfused)
+        out[name] = {"fused_us": round(tf, 2), "standalone_us": round(tp, 2),
+                     "unfused_us": round(tu, 2),
+                     "fused_over_standalone": round(tf / tp, 3),
+                     "unfused_over_fused": round(tu / tf, 3)}
+        del sets, fused, plain, unfused
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, budget_s):

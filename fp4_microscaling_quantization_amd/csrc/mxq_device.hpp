@@ -200,6 +200,35 @@ __device__ __forceinline__ void rotate8(float (&v)[8], int pos)
     }
 }
 
+// ---- block rotation of 16 consecutive positions held by one lane -----------
+// The fp32 butterfly stages of stride 1, 2, 4, 8 inside the lane and, for
+// n = 32, stride 16 across the lane pair (pos, pos ^ 1) at DPP distance 1:
+// the lower lane keeps u + u', the upper one u - u' (u lower, u' upper).
+// No normalisation (the caller multiplies by fl32(1/sqrt(n)) or folds it).
+template <int HN>
+__device__ __forceinline__ void rotate16_raw(float (&v)[16], int pos)
+{
+    if constexpr (HN >= 16) {
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (!(i & s)) {
+                    const float p = v[i], q = v[i + s];
+                    v[i] = p + q;
+                    v[i + s] = p - q;
+                }
+            }
+        }
+        if constexpr (HN == 32) {
+            const float beta = pos ? -1.0f : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = __builtin_fmaf(v[i], beta, lane_xor_f<1>(v[i]));
+        }
+    }
+}
+
 // ---- rounding of 8 signed values y * inv onto the grid --------------------
 // Returns the sign-magnitude nibbles, element i in bits 4i..4i+3.  `r` and
 // `tpb` = 2^(B+1) are only read for SR.

@@ -102,29 +102,12 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
 {
     constexpr int EMAX = GRID == kE2M1 ? 2 : 1;
     // ---- rotation: fp32 butterflies of stride 1, 2, 4, 8 in the lane, 16 across
-    if constexpr (HN >= 16) {
+    rotate16_raw<HN>(v, pos);
+    if constexpr (HN == 32) {
+        const float c = as_f(0x3E3504F3u);  // fl32(1/sqrt(32))
 #pragma unroll
-        for (int s = 1; s < 16; s <<= 1) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (!(i & s)) {
-                    const float p = v[i], q = v[i + s];
-                    v[i] = p + q;
-                    v[i + s] = p - q;
-                }
-            }
-        }
-        if constexpr (HN == 32) {
-            // the lower lane keeps u + u', the upper one u - u' (u lower, u' upper)
-            const float beta = pos ? -1.0f : 1.0f;
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                v[i] = __builtin_fmaf(v[i], beta, lane_xor_f<1>(v[i]));
-            const float c = as_f(0x3E3504F3u);  // fl32(1/sqrt(32))
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                v[i] = v[i] * c;
-        }
+        for (int i = 0; i < 16; ++i)
+            v[i] = v[i] * c;
     }
     // ---- block maximum of |y|
     uint32_t am;

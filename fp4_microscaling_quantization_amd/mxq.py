@@ -22,7 +22,7 @@ AXIS_ROW, AXIS_COL = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 
 SYMBOLS = ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "mxq_bias_stats",
-           "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_rht_sign_mask",
+           "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_rht_sign_mask", "mxq_rotate",
            "mxq_status_string", "mxq_abi_version")
 
 
@@ -69,6 +69,7 @@ def lib() -> C.CDLL:
                                      i64, P]
         L.mxq_gemm_abt.argtypes = L.mxq_wgrad_gemm.argtypes
         L.mxq_rht_sign_mask.argtypes = [C.c_uint64, C.c_uint32]
+        L.mxq_rotate.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, i32, i32, P, i64, P]
         L.mxq_rht_sign_mask.restype = C.c_uint32
         L.mxq_bias_stats.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, i32, C.POINTER(QTensor),
                                      P, P, C.c_size_t, P]
@@ -79,7 +80,7 @@ def lib() -> C.CDLL:
         L.mxq_status_string.restype = C.c_char_p
         L.mxq_abi_version.restype = i32
         for name in ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt",
-                     "mxq_bias_stats", "mxq_round_to_grid"):
+                     "mxq_bias_stats", "mxq_round_to_grid", "mxq_rotate"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -274,6 +275,32 @@ def gemm_abt(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid,
     _check("mxq_gemm_abt", lib().mxq_gemm_abt(C.byref(qa), C.byref(qb), m, n, k, _ptr(c),
                                               c.stride(0), _stream(stream)))
     return c
+
+
+def rotate(x, axis: int, hadamard_n: int, sign_mask: int = 0, out_dtype=OUT_F32, out=None,
+           stream=None):
+    """The block rotation alone, in x's orientation (fp32 or bf16 out)."""
+    import torch
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+    o = torch.empty(x.shape, dtype=dt, device=x.device) if out is None else out
+    cfg = qconfig(hadamard_n=hadamard_n, sign_mask=sign_mask)
+    _check("mxq_rotate", lib().mxq_rotate(C.byref(cfg), _ptr(x), x.shape[0], x.shape[1],
+                                          x.stride(0), axis, out_dtype, _ptr(o), o.stride(0),
+                                          _stream(stream)))
+    return o
+
+
+def prepare_rotate(x, axis: int, hadamard_n: int, sign_mask: int, out_dtype, out, stream=None):
+    """rotate(...) marshalled once into a function of no arguments."""
+    cfg = qconfig(hadamard_n=hadamard_n, sign_mask=sign_mask)
+    args = (C.byref(cfg), _ptr(x), x.shape[0], x.shape[1], x.stride(0), axis, out_dtype, _ptr(out),
+            out.stride(0), _stream(stream))
+    fn = lib().mxq_rotate
+
+    def call():
+        _check("mxq_rotate", fn(*args))
+    call._keep = cfg
+    return call
 
 
 def rht_sign_mask(seed: int, n: int) -> int:

@@ -191,6 +191,22 @@ mxq_status mxq_dequantize(const mxq_qtensor *q, int64_t lines, int64_t k, int32_
 mxq_status mxq_wgrad_gemm(const mxq_qtensor *a, const mxq_qtensor *b, int64_t m, int64_t n,
                           int64_t k, float *c, int64_t ldc, void *stream);
 
+/* The rotation step of mxq_quantize on its own (the first kernel of the
+ * unfused pipeline that the fused quantizer replaces, gist.science summary
+ * "Repensando o Vies de Encolhimento (Shrinkage Bias) no Pre-treinamento de
+ * LLMs em FP4", section "Eficiencia"): y = fl32(1/sqrt(n)) H_n (D x) on every
+ * n-element sub-block of the 32-blocks along `axis` (MXQ_AXIS_ROW: along the
+ * last dimension; MXQ_AXIS_COL: along the first), written to out in x's own
+ * orientation [rows x cols], leading dimension ld_out elements.  out_dtype
+ * MXQ_OUT_F32 gives exactly the values mxq_quantize rounds; MXQ_OUT_BF16
+ * rounds them to nearest even.  cfg->hadamard_n must be 16 or 32 (cfg's
+ * grid / rounding fields are ignored).  Requires the axis length % 32 == 0
+ * and x, out aligned to their element size; 16-byte aligned rows
+ * (out % 16 == 0, ld_out * element size % 16 == 0) take vector stores. */
+mxq_status mxq_rotate(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
+                      int64_t ld_x, int32_t axis, int32_t out_dtype, void *out, int64_t ld_out,
+                      void *stream);
+
 /* The same block-scaled product under its general name, for the three GEMMs
  * of a linear layer in the htx.com news ("Experimento de diagnostico"):
  *   Fprop  Y [T x N]  = X [T x K] W^T:  a = X row-wise,  b = W row-wise
