@@ -147,6 +147,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the bias / SQNR diagnostics")
     ap.add_argument("--no-fusion", action="store_true",
                     help="skip the fused / standalone / unfused quantize comparison")
     ap.add_argument("--copy-calib", action="store_true",
@@ -300,6 +302,9 @@ def main():
         "kernels": kernels,
     }
 
+    if not args.no_quality:
+        rec["quality"] = quality_report(torch, mxq, synth, dev)
+
     if not args.no_fusion:
         rec["fusion"] = fusion_ratios(torch, mxq, synth, dev, max(args.steps, 10))
 
@@ -317,6 +322,110 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, args.cpu_seconds)
 
     print(json.dumps(rec), flush=True)
+
+
+def quality_report(torch, mxq, synth, dev):
+    """What the method does to the numbers, computed by the library's own
+    kernels (mxq_quantize, mxq_bias_stats, mxq_gemm_abt) on the GPU after the
+    timed region:
+      * shrinkage bias and SQNR per workload and grid (RTNE): delta_rel =
+        sum sign(y)(yhat - y) / sum |y| (magnitude-weighted signed error),
+        delta_norm = mean (|yhat| - |y|) / 2^e, SQNR in dB, the saturated
+        fraction, and per grid level the count and mean normalized error;
+      * the SQNR change the H16 rotation brings on the activation workload;
+      * stochastic rounding on the gradient workload over 64 seeds: mean
+        normalized error of the unsaturated elements (expected 0, with its
+        5-sigma bound) and of the saturated ones (clamped, not unbiased);
+      * the weight-gradient output against the fp64 product of the bf16
+        inputs: SQNR and alpha = <C_hat, C> / <C, C> (1 = no shrinkage)."""
+    import math
+    import numpy as np
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def summarize(st):
+        n, ns = st["n"], st["n_saturated"]
+        lc = [int(v) for v in st["level_count"]]
+        return {"delta_rel": st["sum_signed_err"] / st["sum_abs_y"],
+                "delta_norm": st["sum_err_norm"] / n,
+                "sqnr_db": 10.0 * math.log10(st["sum_y2"] / st["sum_err2"]),
+                "saturated_frac": ns / n,
+                "level_count": lc,
+                "level_mean_norm_err": [round(e / c, 5) if c else None
+                                        for e, c in zip(st["level_err_norm"], lc)]}
+
+    def stats(x, axis, **kn):
+        q = mxq.quantize(x, row=axis == 0, col=axis == 1, row_fmt=0, col_fmt=0, **kn)
+        key = "row" if axis == 0 else "col"
+        return mxq.bias_stats(x, axis, q[key][0], q[key][1], 0, **kn)
+
+    grids = {"e2m1": mxq.GRID_E2M1, "e1m2": mxq.GRID_E1M2}
+    rep = {}
+    x1 = to_dev(synth.x_1024())
+    rep["x_1024_row_n0"] = {g: summarize(stats(x1, 0, grid=v)) for g, v in grids.items()}
+    x2 = to_dev(synth.x_8192x4096())
+    r2 = {}
+    for g, v in grids.items():
+        a = summarize(stats(x2, 0, grid=v))
+        b = summarize(stats(x2, 0, grid=v, hadamard_n=16))
+        r2[g] = {"n0": a, "h16": b, "delta_sqnr_db": b["sqnr_db"] - a["sqnr_db"]}
+    rep["x_8192x4096_row"] = r2
+    del x1, x2
+    w = to_dev(synth.w_14336x4096())
+    ws = synth.sign_mask(synth.SIGNS_W, 32)
+    rep["w_14336x4096_h32_signs"] = {
+        g: {"row": summarize(stats(w, 0, grid=v, hadamard_n=32, sign_mask=ws)),
+            "col": summarize(stats(w, 1, grid=v, hadamard_n=32, sign_mask=ws))}
+        for g, v in grids.items()}
+    del w
+    dy = to_dev(synth.dy_16384x4096())
+    ds = synth.sign_mask(synth.SIGNS_DY, 16)
+    r4 = {g: summarize(stats(dy, 1, grid=v, hadamard_n=16, sign_mask=ds)) for g, v in grids.items()}
+    tot = tot_sat = 0.0
+    n_unsat = n_sat = 0
+    for seed in range(64):
+        st = stats(dy, 1, grid=mxq.GRID_E1M2, round=mxq.SR, hadamard_n=16, sign_mask=ds,
+                   sr_seed=seed)
+        tot += st["sum_err_norm"] - st["sum_err_norm_sat"]
+        tot_sat += st["sum_err_norm_sat"]
+        n_unsat += st["n"] - st["n_saturated"]
+        n_sat += st["n_saturated"]
+    r4["e1m2_sr_64_seeds"] = {"unsaturated_mean_norm_err": tot / n_unsat,
+                              "five_sigma_bound": 5 * 0.25 / math.sqrt(n_unsat),
+                              "saturated_mean_norm_err": tot_sat / n_sat if n_sat else None,
+                              "saturated_frac": n_sat / (n_sat + n_unsat)}
+    rep["dy_16384x4096_col_h16_signs"] = r4
+    del dy
+    # weight-gradient output quality, both operand variants
+    dyw, xw = to_dev(synth.dy_8192x4096()), to_dev(synth.x_wgrad_8192x4096())
+    ref = dyw.double().t().contiguous() @ xw.double()
+    sg = synth.sign_mask(synth.SIGNS_WGRAD, 16)
+    r5 = {}
+    for name, g, f in (("e1m2_e2m3", mxq.GRID_E1M2, mxq.FMT_E2M3), ("e2m1_fp4", mxq.GRID_E2M1, mxq.FMT_FP4)):
+        qd = mxq.quantize(dyw, grid=g, round=mxq.SR, hadamard_n=16, sign_mask=sg,
+                          sr_seed=synth.SR_SEED_WGRAD, row=False, col=True, col_fmt=f,
+                          col_layout=mxq.LAYOUT_MFMA)["col"]
+        qx = mxq.quantize(xw, grid=g, hadamard_n=16, sign_mask=sg, row=False, col=True,
+                          col_fmt=f, col_layout=mxq.LAYOUT_MFMA)["col"]
+        c = mxq.gemm_abt(qd[0], qd[1], f, g, qx[0], qx[1], f, g, layout=mxq.LAYOUT_MFMA,
+                         m=4096, n=4096, k=8192).double()
+        err = c - ref
+        r5[name] = {"sqnr_db": 10.0 * math.log10(float((ref * ref).sum()) / float((err * err).sum())),
+                    "alpha": float((c * ref).sum() / (ref * ref).sum())}
+    rep["wgrad_8192_dW_vs_fp64"] = r5
+    del dyw, xw, ref
+    torch.cuda.empty_cache()
+
+    def rnd(o):
+        if isinstance(o, float):
+            return float(f"{o:.6g}")
+        if isinstance(o, dict):
+            return {k: rnd(v) for k, v in o.items()}
+        if isinstance(o, list):
+            return [rnd(v) for v in o]
+        return o
+    return rnd(rep)
 
 
 def fusion_ratios(torch, mxq, synth, dev, reps):
