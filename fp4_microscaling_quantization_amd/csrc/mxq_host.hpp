@@ -25,4 +25,18 @@ struct ColLaunch {
 };
 hipError_t launch_quant_col(int grid, int round, int hn, const ColLaunch &q);
 
+// Launch of the row-wise-only quantize kernel (two lanes per block).
+struct RowLaunch {
+    const uint16_t *x;
+    uint64_t nblocks;  // rows * cols / 32
+    uint32_t nbr;      // blocks per row
+    int64_t ld;
+    int dense;         // ld == cols
+    int vec;           // x 16-byte aligned and ld % 8 == 0: 128-bit loads
+    OutDesc out;
+    QKnobs kn;
+    hipStream_t s;
+};
+hipError_t launch_quant_row16(int grid, int round, int hn, const RowLaunch &q);
+
 }  // namespace mxq

@@ -1,12 +1,10 @@
 // Fused block-Hadamard rotation + MX block-32 quantization kernels (gfx950)
 // and the host side of mxq_quantize / mxq_round_to_grid.
 //
-// Two kernels:
-//  * k_quant_row: blocks along the contiguous dimension.  4 lanes per block,
-//    8 bf16 per lane (one 128-bit load), consecutive quads on consecutive
-//    blocks, so each wave reads 1 KiB and writes 256 B of codes contiguously.
-//  * k_quant_tile: blocks along rows (written transposed), optionally the
-//    row-wise output too from the same registers.  Each lane loads an 8x8
+// k_quant_tile writes both outputs from one read: blocks along rows (written
+// transposed) and blocks along the contiguous dimension.  (Calls asking for
+// one output go to k_quant_row16 / k_quant_col, quantize_col.hip.)  Each lane
+// loads an 8x8
 //    bf16 tile (8 rows x 128-bit); a 16-lane DPP row covers 32x32, so the
 //    4 lanes of a column block (xor 1, 2) and of a row block (xor 4, 8) are
 //    both reachable by DPP without going through LDS.
@@ -22,8 +20,6 @@
 #include "quant_out.hpp"
 
 namespace mxq {
-
-constexpr int kRowU = 4;  // blocks per quad in one k_quant_row workgroup
 
 // Widen 8 bf16 (one uint4) to fp32 and flip the signs whose bit is set in `sg`.
 __device__ __forceinline__ void widen8(const uint4 &q, uint32_t sg, float (&v)[8])
@@ -71,49 +67,6 @@ __device__ __forceinline__ void store_slice(const OutDesc &o, uint64_t line, uin
     }
     if (valid && pos == 0)
         o.scales[scale_offset(o, line, jb)] = (uint8_t)sc;
-}
-
-template <int GRID, int ROUND, int HN>
-__global__ __launch_bounds__(256) void k_quant_row(const uint16_t *__restrict__ x, uint64_t nblocks,
-                                                   uint32_t nbr, int64_t ld, int dense, int vec,
-                                                   OutDesc out, QKnobs kn)
-{
-    const int t = threadIdx.x, pos = t & 3;
-    const uint64_t b0 = (uint64_t)blockIdx.x * (64 * kRowU) + (uint64_t)(t >> 2);
-    const uint32_t sg = HN ? (kn.sign_mask >> ((8 * pos) % (HN ? HN : 32))) & 0xFFu : 0u;
-    uint4 raw[kRowU];
-#pragma unroll
-    for (int u = 0; u < kRowU; ++u) {
-        const uint64_t b = b0 + 64u * u;
-        raw[u] = make_uint4(0, 0, 0, 0);
-        if (b < nblocks) {
-            int64_t off;
-            if (dense) {
-                off = (int64_t)b * 32 + 8 * pos;
-            } else {
-                const uint64_t r = b / nbr;
-                off = (int64_t)r * ld + (int64_t)(b - r * nbr) * 32 + 8 * pos;
-            }
-            raw[u] = vec ? *reinterpret_cast<const uint4 *>(x + off) : load8_scalar(x + off);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < kRowU; ++u) {
-        const uint64_t b = b0 + 64u * u;
-        float v[8];
-        widen8(raw[u], sg, v);
-        uint32_t sc;
-        const uint32_t w = quant8<GRID, ROUND, HN, 1, 2>(v, pos, b, kn, &sc);
-        uint64_t line = 0, jb = b;
-        if (out.layout != MXQ_LAYOUT_ROWS) {
-            line = b / nbr;
-            jb = b - line * nbr;
-        }
-        if (out.layout == MXQ_LAYOUT_ROWS)
-            store_slice<GRID, 1>(out, 0, b, pos, w, sc, b < nblocks);   // line 0, block b == line*nbr+jb
-        else
-            store_slice<GRID, 1>(out, line, jb, pos, w, sc, b < nblocks);
-    }
 }
 
 template <int GRID, int ROUND, int HN, bool ROWS, bool COLS>
@@ -222,23 +175,10 @@ struct QuantLaunch {
 template <int GRID, int ROUND, int HN>
 hipError_t launch_quant(const QuantLaunch &q)
 {
-    const bool rows_out = q.has_row, cols_out = q.has_col;
-    if (rows_out && !cols_out) {
-        const uint64_t nbr = (uint64_t)q.cols / 32;
-        const uint64_t nblocks = (uint64_t)q.rows * nbr;
-        const uint64_t grid = (nblocks + 64 * kRowU - 1) / (64 * kRowU);
-        hipLaunchKernelGGL((k_quant_row<GRID, ROUND, HN>), dim3((unsigned)grid), dim3(256), 0, q.s,
-                           q.x, nblocks, (uint32_t)nbr, q.ld, (int)(q.ld == q.cols), q.vec,
-                           q.rout, q.kn);
-    } else {
-        const dim3 grid((unsigned)((q.cols + 127) / 128), (unsigned)((q.rows + 127) / 128));
-        if (rows_out)
-            hipLaunchKernelGGL((k_quant_tile<GRID, ROUND, HN, true, true>), grid, dim3(256), 0, q.s,
-                               q.x, q.rows, q.cols, q.ld, q.rout, q.cout, q.vec, q.kn);
-        else
-            hipLaunchKernelGGL((k_quant_tile<GRID, ROUND, HN, false, true>), grid, dim3(256), 0,
-                               q.s, q.x, q.rows, q.cols, q.ld, q.rout, q.cout, q.vec, q.kn);
-    }
+    // both outputs from one read (row-only and column-only calls have kernels of their own)
+    const dim3 grid((unsigned)((q.cols + 127) / 128), (unsigned)((q.rows + 127) / 128));
+    hipLaunchKernelGGL((k_quant_tile<GRID, ROUND, HN, true, true>), grid, dim3(256), 0, q.s, q.x,
+                       q.rows, q.cols, q.ld, q.rout, q.cout, q.vec, q.kn);
     return hipGetLastError();
 }
 
@@ -350,7 +290,12 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
     q.s = static_cast<hipStream_t>(stream);
 
     hipError_t e;
-    if (!row_out) {
+    if (!col_out) {
+        const uint64_t nbr = (uint64_t)cols / 32;
+        RowLaunch r{q.x, (uint64_t)rows * nbr, (uint32_t)nbr, ld_x, ld_x == cols ? 1 : 0, q.vec,
+                    q.rout, q.kn, q.s};
+        e = launch_quant_row16(cfg->grid, cfg->round, cfg->hadamard_n, r);
+    } else if (!row_out) {
         ColLaunch c{q.x, rows, cols, ld_x, q.cout,
                     (reinterpret_cast<uintptr_t>(x) % 8 == 0 && ld_x % 4 == 0) ? 1 : 0, q.kn, q.s};
         e = launch_quant_col(cfg->grid, cfg->round, cfg->hadamard_n, c);

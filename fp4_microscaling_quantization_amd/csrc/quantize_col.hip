@@ -371,7 +371,122 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
     }
 }
 
+// Row-wise fused rotate + quantize with the column kernel's per-lane work:
+// two lanes per 32-block, each holding 16 consecutive positions (two 16-byte
+// loads), the lane pair adjacent (DPP distance 1).  A wave handles 128
+// consecutive blocks of the row-major block order as 4 rounds of 32 (so each
+// load instruction reads 2 KB contiguously when rows are dense), a lane 4
+// blocks; codes go out as 8 (FP4) or 12 (E2M3) contiguous bytes per lane.
+template <int GRID, int ROUND, int HN, int FMT>
+__global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict__ x,
+                                                     uint64_t nblocks, uint32_t nbr, int64_t ld,
+                                                     int dense, int vec, OutDesc out, QKnobs kn)
+{
+    constexpr int U = 4;
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int pos = lane & 1, pr = lane >> 1;
+    const uint64_t base = ((uint64_t)blockIdx.x * 4 + wv) * (32 * U);
+    const uint32_t sg = HN == 16 ? kn.sign_mask : HN == 32 ? kn.sign_mask >> (16 * pos) : 0u;
+    const float h = kn.sr_bits == 16 ? 0x1p-17f : 0x1p-9f;  // 2^-(B+1)
+    const float h2 = 2.0f * h;
+    constexpr bool kExact = FMT == MXQ_FMT_E2M3;
+
+    float v[U][16];
+    uint64_t line[U], jbk[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint64_t b = base + 32 * u + pr;
+        const bool ok = b < nblocks;
+        line[u] = ok ? b / nbr : 0;
+        jbk[u] = ok ? b - line[u] * nbr : 0;
+        const int64_t off = (dense ? (int64_t)b * 32 : (int64_t)line[u] * ld + (int64_t)jbk[u] * 32) + 16 * pos;
+        uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (ok) {
+            if (vec) {
+                const uint4 q0 = *reinterpret_cast<const uint4 *>(x + off);
+                const uint4 q1 = *reinterpret_cast<const uint4 *>(x + off + 8);
+                w[0] = q0.x; w[1] = q0.y; w[2] = q0.z; w[3] = q0.w;
+                w[4] = q1.x; w[5] = q1.y; w[6] = q1.z; w[7] = q1.w;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    w[k] = (uint32_t)x[off + 2 * k] | ((uint32_t)x[off + 2 * k + 1] << 16);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            v[u][2 * k] = as_f((w[k] << 16) ^ (((sg >> (2 * k)) & 1u) << 31));
+            v[u][2 * k + 1] = as_f((w[k] & 0xFFFF0000u) ^ (((sg >> (2 * k + 1)) & 1u) << 31));
+        }
+    }
+#pragma unroll
+    for (int up = 0; up < U; up += 2) {
+        uint32_t sc[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            sc[d] = col16<GRID, ROUND, HN, kExact>(v[up + d], pos, base + 32 * (up + d) + pr, kn, h, h2);
+        if constexpr (FMT == MXQ_FMT_E2M3) {
+            f16v s0, s1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s0[j] = v[up][2 * j];
+                s1[j] = v[up][2 * j + 1];
+                s0[8 + j] = v[up + 1][2 * j];
+                s1[8 + j] = v[up + 1][2 * j + 1];
+            }
+            uint32_t o[6];
+            cvt_e2m3_32(s0, s1, level_unit<GRID, ROUND>(), o);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                if (base + 32 * (up + d) + pr >= nblocks)
+                    continue;
+                uint32_t wd[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    wd[k] = sc[d] == 0xFFu ? 0u : o[3 * d + k];
+                store_words<3>(out, line[up + d], jbk[up + d], pos, wd);
+            }
+        } else {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                uint32_t wd[2];
+                pack_fp4<GRID, ROUND>(v[up + d], sc[d], wd);
+                if (base + 32 * (up + d) + pr < nblocks)
+                    store_words<2>(out, line[up + d], jbk[up + d], pos, wd);
+            }
+        }
+        if (pos == 0) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+                if (base + 32 * (up + d) + pr < nblocks)
+                    out.scales[scale_offset(out, line[up + d], jbk[up + d])] = (uint8_t)sc[d];
+        }
+    }
+}
+
 namespace {
+
+template <int GRID, int ROUND, int HN>
+void launch_row16_fmt(const RowLaunch &q)
+{
+    const unsigned grid = (unsigned)((q.nblocks + 511) / 512);
+    if (q.out.fmt == MXQ_FMT_E2M3)
+        hipLaunchKernelGGL((k_quant_row16<GRID, ROUND, HN, MXQ_FMT_E2M3>), dim3(grid), dim3(256),
+                           0, q.s, q.x, q.nblocks, q.nbr, q.ld, q.dense, q.vec, q.out, q.kn);
+    else
+        hipLaunchKernelGGL((k_quant_row16<GRID, ROUND, HN, MXQ_FMT_FP4>), dim3(grid), dim3(256),
+                           0, q.s, q.x, q.nblocks, q.nbr, q.ld, q.dense, q.vec, q.out, q.kn);
+}
+
+template <int GRID, int ROUND>
+void launch_row16_hn(int hn, const RowLaunch &q)
+{
+    switch (hn) {
+    case 0: launch_row16_fmt<GRID, ROUND, 0>(q); break;
+    case 16: launch_row16_fmt<GRID, ROUND, 16>(q); break;
+    default: launch_row16_fmt<GRID, ROUND, 32>(q); break;
+    }
+}
 
 template <int GRID, int ROUND, int HN>
 void launch_col_fmt(const ColLaunch &q)
@@ -396,6 +511,15 @@ void launch_col_hn(int hn, const ColLaunch &q)
 }
 
 }  // namespace
+
+hipError_t launch_quant_row16(int grid, int round, int hn, const RowLaunch &q)
+{
+    if (grid == kE2M1)
+        round == kRTNE ? launch_row16_hn<kE2M1, kRTNE>(hn, q) : launch_row16_hn<kE2M1, kSR>(hn, q);
+    else
+        round == kRTNE ? launch_row16_hn<kE1M2, kRTNE>(hn, q) : launch_row16_hn<kE1M2, kSR>(hn, q);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_col(int grid, int round, int hn, const ColLaunch &q)
 {
