@@ -88,28 +88,6 @@ __device__ __forceinline__ Rand4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     return r;
 }
 
-// Random bits of the 8 positions 8*pos .. 8*pos+7 of block `blk`.
-__device__ __forceinline__ void sr_bits8(const QKnobs &kn, int pos, uint64_t blk, uint32_t (&r)[8])
-{
-    const uint32_t blo = (uint32_t)blk, bhi = (uint32_t)(blk >> 32);
-    if (kn.sr_bits == 16) {
-        // counter word 0 = j >> 3 = pos; element i uses half (i&1) of word i>>1
-        Rand4 q = philox4x32_10((uint32_t)pos, blo, bhi, kn.stream, kn.seed_lo, kn.seed_hi);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            r[i] = (q.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu;
-    } else {
-        // counter word 0 = j >> 4 = pos >> 1; element j = 8 pos + i uses byte
-        // (j & 3) of word ((j >> 2) & 3) = 2 (pos & 1) + (i >> 2)
-        Rand4 q = philox4x32_10((uint32_t)(pos >> 1), blo, bhi, kn.stream, kn.seed_lo, kn.seed_hi);
-        const uint32_t wa = (pos & 1) ? q.w[2] : q.w[0];
-        const uint32_t wb = (pos & 1) ? q.w[3] : q.w[1];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            r[i] = (((i < 4) ? wa : wb) >> (8 * (i & 3))) & 0xFFu;
-    }
-}
-
 // ---- rounding of a normalized magnitude a = |y| 2^-e (0 <= a < 2^(emax+1)) --
 // E1M2 levels 0.5 m: m = RNE(2a) by one fused multiply-add against 2^23
 // (single rounding of the exact 2a), saturated at 7.
@@ -257,64 +235,6 @@ __device__ __forceinline__ uint32_t round8(const float (&v)[8], float inv, const
         }
     }
     return w;
-}
-
-// ---- the 8-element slice of one block ---------------------------------------
-// v: this lane's 8 values (bf16 already widened, sign mask already applied).
-// Returns the 8 sign-magnitude nibbles packed little-endian (position 8*pos+i
-// in bits 4i..4i+3); *scale receives the block's E8M0 code (all 4 lanes).
-template <int GRID, int ROUND, int HN, int XA, int XB>
-__device__ __forceinline__ uint32_t quant8(float (&v)[8], int pos, uint64_t blk, const QKnobs &kn,
-                                           uint32_t *scale)
-{
-    constexpr int EMAX = GRID == kE2M1 ? 2 : 1;
-    rotate8<HN, XA, XB>(v, pos);
-    // Block maximum of |y| as an unsigned compare of the magnitude bits: NaN
-    // patterns exceed Inf, which exceeds every finite value.
-    uint32_t am = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        am = max(am, as_u(v[i]) & 0x7FFFFFFFu);
-    am = max(am, lane_xor<XA>(am));
-    am = max(am, lane_xor<XB>(am));
-    // e = floor(log2 amax) - EMAX, clamped at -127; code e + 127.  For a
-    // normal amax floor(log2) is its biased exponent - 127; a zero or
-    // subnormal amax gives e <= -127 - EMAX, i.e. code 0.
-    const uint32_t sc = am >= 0x7F800000u ? 0xFFu : (uint32_t)max((int)(am >> 23) - EMAX, 0);
-    *scale = sc;
-    const float inv = as_f((254u - min(sc, 253u)) << 23);      // 2^-e, exact
-
-    uint32_t r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    float tpb = 0.f;
-    if constexpr (ROUND == kSR) {
-        sr_bits8(kn, pos, blk, r);
-        tpb = kn.sr_bits == 16 ? 131072.0f : 512.0f;           // 2^(B+1)
-    }
-    const uint32_t w = round8<GRID, ROUND>(v, inv, r, tpb);
-    return sc == 0xFFu ? 0u : w;
-}
-
-// FP6 E2M3 code of a nibble (value-preserving): E2M1 level m is E2M3 code
-// 4m; E1M2 level 0.5 m is 4m below 2 and 2m + 8 from 2 up.  Sign to bit 5.
-template <int GRID>
-__device__ __forceinline__ uint32_t e2m3_of_nibble(uint32_t nib)
-{
-    const uint32_t m = nib & 7u, s = (nib & 8u) << 2;
-    if constexpr (GRID == kE2M1)
-        return s | (m << 2);
-    else
-        return s | (m < 4u ? (m << 2) : (2u * m + 8u));
-}
-
-// Pack 8 nibbles into 8 E2M3 codes: 48 bits, element i at bits 6i.
-template <int GRID>
-__device__ __forceinline__ uint64_t e2m3_pack8(uint32_t w)
-{
-    uint64_t acc = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        acc |= (uint64_t)e2m3_of_nibble<GRID>((w >> (4 * i)) & 15u) << (6 * i);
-    return acc;
 }
 
 }  // namespace mxq

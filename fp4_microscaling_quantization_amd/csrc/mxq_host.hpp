@@ -39,4 +39,15 @@ struct RowLaunch {
 };
 hipError_t launch_quant_row16(int grid, int round, int hn, const RowLaunch &q);
 
+// Launch of the kernel that writes both outputs from one read.
+struct DualLaunch {
+    const uint16_t *x;
+    int64_t rows, cols, ld;
+    OutDesc rout, cout;
+    int vec;  // x 8-byte aligned and ld % 4 == 0: 64-bit loads
+    QKnobs kn;
+    hipStream_t s;
+};
+hipError_t launch_quant_dual16(int grid, int round, int hn, const DualLaunch &q);
+
 }  // namespace mxq

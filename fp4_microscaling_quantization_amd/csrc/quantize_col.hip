@@ -231,17 +231,43 @@ __device__ __forceinline__ void store_words(const OutDesc &o, uint64_t line, uin
         d[k] = w[k];
 }
 
-// The same words into the LDS image of a workgroup's MFMA-layout run: column
-// cl (0..127) of the tile, row band wv (0..3, i.e. block 4 by + wv).
+// The same words into the LDS image of a workgroup's 128 column x 4 block
+// output tile: column cl (0..127), row band wv (0..3, i.e. block 4 by + wv).
+// MFMA layout: the 8 tiles x 64 lane slots of one k-step (one contiguous run);
+// row layout: column-major, each column's 4 blocks adjacent (one run each).
 template <int N>
-__device__ __forceinline__ void stage_words(uint32_t *stage, int cl, int wv, int pos,
+__device__ __forceinline__ void stage_words(uint32_t *stage, int layout, int cl, int wv, int pos,
                                             const uint32_t *w)
 {
-    const int slot = (cl >> 4) * 64 + 16 * wv + (cl & 15);
+    const int slot = layout == MXQ_LAYOUT_MFMA ? (cl >> 4) * 64 + 16 * wv + (cl & 15) : 4 * cl + wv;
     uint32_t *d = stage + slot * (2 * N) + N * pos;
 #pragma unroll
     for (int k = 0; k < N; ++k)
         d[k] = w[k];
+}
+
+// Write the staged output tile (after a barrier): line0 = 128 bx, block 4 by.
+template <int BB>
+__device__ __forceinline__ void flush_stage(const OutDesc &o, const uint32_t *stage, int t,
+                                            uint64_t line0, uint64_t jb0)
+{
+    if (o.layout == MXQ_LAYOUT_MFMA) {
+        // one run of 128 * BB bytes, 16-byte aligned
+        uint4 *dst = reinterpret_cast<uint4 *>(o.codes + code_offset(o, line0, jb0, BB));
+        const uint4 *src = reinterpret_cast<const uint4 *>(stage);
+#pragma unroll
+        for (int k = 0; k < BB / 8; ++k)
+            dst[k * 256 + t] = src[k * 256 + t];
+    } else {
+        // 128 runs of 4 * BB bytes (codes are only 4-byte aligned here)
+        constexpr int W = BB;              // words per column run (4 blocks x BB / 4)
+#pragma unroll
+        for (int k = 0; k < W / 2; ++k) {
+            const int idx = k * 256 + t, cl = idx / W, q = idx % W;
+            reinterpret_cast<uint32_t *>(o.codes + code_offset(o, line0 + cl, jb0, BB))[q] =
+                stage[cl * W + q];
+        }
+    }
 }
 
 template <int GRID, int ROUND, int HN, int FMT>
@@ -252,12 +278,13 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int pos = lane & 1, cg = lane >> 1;
     const int64_t rband = (int64_t)blockIdx.y * 128 + wv * 32;  // rows % 32 == 0
-    // In the MFMA layout (rows % 128 == 0) a full 128-column tile's codes form
-    // one contiguous run: stage them in LDS and write the run with 16-byte
-    // stores.  Every wave of such a workgroup has rows, so none returns early.
+    // A full 128 x 128 tile stages its codes in LDS and writes them as long
+    // runs (MFMA layout: one run; row layout: 4 blocks per column).  Every wave
+    // of such a workgroup has rows, so none returns early.
     constexpr int BB = FMT == MXQ_FMT_E2M3 ? 24 : 16;           // bytes per block
-    __shared__ uint32_t stage[128 * BB];                         // 8 tiles x 64 slots
-    const bool staged = out.layout == MXQ_LAYOUT_MFMA && (int64_t)blockIdx.x * 128 + 128 <= cols;
+    __shared__ uint32_t stage[128 * BB];                         // 128 columns x 4 blocks
+    const bool staged = (int64_t)blockIdx.x * 128 + 128 <= cols &&
+                        (int64_t)blockIdx.y * 128 + 128 <= rows;
     if (rband >= rows)
         return;                                                   // whole wave
     const int64_t r0 = rband + 16 * pos;
@@ -329,8 +356,8 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
                 o[3 + k] = sb == 0xFFu ? 0u : o[3 + k];
             }
             if (staged) {
-                stage_words<3>(stage, 4 * cg + 2 * jp, wv, pos, o);
-                stage_words<3>(stage, 4 * cg + 2 * jp + 1, wv, pos, o + 3);
+                stage_words<3>(stage, out.layout, 4 * cg + 2 * jp, wv, pos, o);
+                stage_words<3>(stage, out.layout, 4 * cg + 2 * jp + 1, wv, pos, o + 3);
             } else {
                 if (ca < cols)
                     store_words<3>(out, (uint64_t)ca, jb, pos, o);
@@ -342,8 +369,8 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
             pack_fp4<GRID, ROUND>(a, sa, wa);
             pack_fp4<GRID, ROUND>(b, sb, wb);
             if (staged) {
-                stage_words<2>(stage, 4 * cg + 2 * jp, wv, pos, wa);
-                stage_words<2>(stage, 4 * cg + 2 * jp + 1, wv, pos, wb);
+                stage_words<2>(stage, out.layout, 4 * cg + 2 * jp, wv, pos, wa);
+                stage_words<2>(stage, out.layout, 4 * cg + 2 * jp + 1, wv, pos, wb);
             } else {
                 if (ca < cols)
                     store_words<2>(out, (uint64_t)ca, jb, pos, wa);
@@ -359,15 +386,8 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
         }
     }
     if (staged) {
-        // the workgroup's 4 row bands are the 4 lane groups of one k-step: the
-        // 8 tiles x 64 slots of that step start at line 128 bx, block 4 by
         __syncthreads();
-        uint4 *dst = reinterpret_cast<uint4 *>(
-            out.codes + code_offset(out, (uint64_t)blockIdx.x * 128, (uint64_t)blockIdx.y * 4, BB));
-        const uint4 *src = reinterpret_cast<const uint4 *>(stage);
-#pragma unroll
-        for (int k = 0; k < BB / 8; ++k)
-            dst[k * 256 + t] = src[k * 256 + t];
+        flush_stage<BB>(out, stage, t, (uint64_t)blockIdx.x * 128, (uint64_t)blockIdx.y * 4);
     }
 }
 
@@ -464,7 +484,233 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
     }
 }
 
+// Both outputs from one read.  Phase 1 is k_quant_col's work on the tile
+// (column blocks, 16 rows x 4 columns per lane); each lane also stores its raw
+// bf16 words into an LDS image of the 128 x 128 tile.  After one barrier,
+// phase 2 reads the tile's rows back from LDS and runs the row kernel's work
+// on them (two lanes per row block, 16 consecutive columns each).  The LDS
+// row stride is 264 bytes: the two 16-row halves a wave writes at once then
+// fall 32 banks apart.
+constexpr int kTileRS = 264;   // LDS bytes per tile row (128 bf16 + 8 pad)
+
+template <int GRID, int ROUND, int HN, int FMTR, int FMTC>
+__global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict__ x, int64_t rows,
+                                                      int64_t cols, int64_t ld, OutDesc rout,
+                                                      OutDesc cout, int vec, QKnobs kn)
+{
+    constexpr int BBC = FMTC == MXQ_FMT_E2M3 ? 24 : 16;
+    __shared__ __align__(16) uint8_t tile[128 * kTileRS];
+    __shared__ uint32_t stage[128 * BBC];
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int pos = lane & 1, cg = lane >> 1;
+    const int64_t row0 = (int64_t)blockIdx.y * 128, col0 = (int64_t)blockIdx.x * 128;
+    const int64_t rband = row0 + wv * 32;                         // rows % 32 == 0
+    const bool live = rband < rows;                               // whole wave
+    const bool staged = col0 + 128 <= cols && row0 + 128 <= rows;
+    const float h = kn.sr_bits == 16 ? 0x1p-17f : 0x1p-9f;
+    const float h2 = 2.0f * h;
+
+    // ---- phase 1: load, stash, column blocks
+    if (live) {
+        const int64_t r0 = rband + 16 * pos;
+        const int64_t c0 = col0 + 4 * cg;
+        const uint64_t jb = (uint64_t)rband >> 5, nbc = (uint64_t)rows >> 5;
+        uint32_t lo[16], hi[16];
+        if (vec && c0 + 4 <= cols) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint2 w = *reinterpret_cast<const uint2 *>(x + (r0 + i) * ld + c0);
+                lo[i] = w.x;
+                hi[i] = w.y;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                uint32_t hh[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    hh[j] = (c0 + j < cols) ? (uint32_t)x[(r0 + i) * ld + c0 + j] : 0u;
+                lo[i] = hh[0] | (hh[1] << 16);
+                hi[i] = hh[2] | (hh[3] << 16);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            *reinterpret_cast<uint2 *>(tile + (32 * wv + 16 * pos + i) * kTileRS + 8 * cg) =
+                make_uint2(lo[i], hi[i]);
+        if constexpr (HN > 0) {
+            const uint32_t sg = HN == 16 ? kn.sign_mask : kn.sign_mask >> (16 * pos);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t f = ((sg >> i) & 1u) ? 0x80008000u : 0u;
+                lo[i] ^= f;
+                hi[i] ^= f;
+            }
+        }
+        constexpr bool kExact = FMTC == MXQ_FMT_E2M3;
+#pragma unroll
+        for (int jp = 0; jp < 2; ++jp) {
+            float a[16], b[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t w = jp ? hi[i] : lo[i];
+                a[i] = as_f(w << 16);
+                b[i] = as_f(w & 0xFFFF0000u);
+            }
+            const int64_t ca = c0 + 2 * jp, cb = ca + 1;
+            const uint32_t sa = col16<GRID, ROUND, HN, kExact>(a, pos, (uint64_t)ca * nbc + jb, kn, h, h2);
+            const uint32_t sb = col16<GRID, ROUND, HN, kExact>(b, pos, (uint64_t)cb * nbc + jb, kn, h, h2);
+            uint32_t wa[3], wb[3];
+            if constexpr (FMTC == MXQ_FMT_E2M3) {
+                f16v s0, s1;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    s0[j] = a[2 * j];
+                    s1[j] = a[2 * j + 1];
+                    s0[8 + j] = b[2 * j];
+                    s1[8 + j] = b[2 * j + 1];
+                }
+                uint32_t o[6];
+                cvt_e2m3_32(s0, s1, level_unit<GRID, ROUND>(), o);
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    wa[k] = sa == 0xFFu ? 0u : o[k];
+                    wb[k] = sb == 0xFFu ? 0u : o[3 + k];
+                }
+            } else {
+                uint32_t pa[2], pb[2];
+                pack_fp4<GRID, ROUND>(a, sa, pa);
+                pack_fp4<GRID, ROUND>(b, sb, pb);
+                wa[0] = pa[0]; wa[1] = pa[1]; wb[0] = pb[0]; wb[1] = pb[1];
+            }
+            constexpr int N = BBC / 8;
+            if (staged) {
+                stage_words<N>(stage, cout.layout, 4 * cg + 2 * jp, wv, pos, wa);
+                stage_words<N>(stage, cout.layout, 4 * cg + 2 * jp + 1, wv, pos, wb);
+            } else {
+                if (ca < cols)
+                    store_words<N>(cout, (uint64_t)ca, jb, pos, wa);
+                if (cb < cols)
+                    store_words<N>(cout, (uint64_t)cb, jb, pos, wb);
+            }
+            if (pos == 0) {
+                if (ca < cols)
+                    cout.scales[scale_offset(cout, (uint64_t)ca, jb)] = (uint8_t)sa;
+                if (cb < cols)
+                    cout.scales[scale_offset(cout, (uint64_t)cb, jb)] = (uint8_t)sb;
+            }
+        }
+    }
+    __syncthreads();
+    if (staged)
+        flush_stage<BBC>(cout, stage, t, (uint64_t)col0, (uint64_t)blockIdx.y * 4);
+
+    // ---- phase 2: row blocks of the tile from LDS: 128 rows x 4 blocks; lane pair
+    // p = t >> 1 takes block p % 4 of rows p / 4 + 32 u, u = 0..3
+    const uint64_t nbr = (uint64_t)cols >> 5;
+    const int p = t >> 1;
+    const uint32_t sgr = HN == 16 ? kn.sign_mask : HN == 32 ? kn.sign_mask >> (16 * pos) : 0u;
+    constexpr bool kExactR = FMTR == MXQ_FMT_E2M3;
+    float v[4][16];
+    bool ok[4];
+    uint64_t rline[4], rjb[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int lr = p / 4 + 32 * u, lb = p % 4;
+        rline[u] = (uint64_t)(row0 + lr);
+        rjb[u] = (uint64_t)(col0 / 32 + lb);
+        ok[u] = (int64_t)rline[u] < rows && rjb[u] < nbr;
+        const uint2 *src = reinterpret_cast<const uint2 *>(tile + lr * kTileRS + 64 * lb + 32 * pos);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint2 w = src[k];
+            const uint32_t wd[2] = {w.x, w.y};
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int i = 4 * k + 2 * e;
+                v[u][i] = as_f((wd[e] << 16) ^ (((sgr >> i) & 1u) << 31));
+                v[u][i + 1] = as_f((wd[e] & 0xFFFF0000u) ^ (((sgr >> (i + 1)) & 1u) << 31));
+            }
+        }
+    }
+#pragma unroll
+    for (int up = 0; up < 4; up += 2) {
+        uint32_t sc[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            sc[d] = col16<GRID, ROUND, HN, kExactR>(v[up + d], pos,
+                                                    rline[up + d] * nbr + rjb[up + d], kn, h, h2);
+        if constexpr (FMTR == MXQ_FMT_E2M3) {
+            f16v s0, s1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s0[j] = v[up][2 * j];
+                s1[j] = v[up][2 * j + 1];
+                s0[8 + j] = v[up + 1][2 * j];
+                s1[8 + j] = v[up + 1][2 * j + 1];
+            }
+            uint32_t o[6];
+            cvt_e2m3_32(s0, s1, level_unit<GRID, ROUND>(), o);
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                if (!ok[up + d])
+                    continue;
+                uint32_t wd[3];
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    wd[k] = sc[d] == 0xFFu ? 0u : o[3 * d + k];
+                store_words<3>(rout, rline[up + d], rjb[up + d], pos, wd);
+            }
+        } else {
+#pragma unroll
+            for (int d = 0; d < 2; ++d) {
+                uint32_t wd[2];
+                pack_fp4<GRID, ROUND>(v[up + d], sc[d], wd);
+                if (ok[up + d])
+                    store_words<2>(rout, rline[up + d], rjb[up + d], pos, wd);
+            }
+        }
+        if (pos == 0) {
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+                if (ok[up + d])
+                    rout.scales[scale_offset(rout, rline[up + d], rjb[up + d])] = (uint8_t)sc[d];
+        }
+    }
+}
+
 namespace {
+
+template <int GRID, int ROUND, int HN, int FR>
+void launch_dual_fc(const DualLaunch &q)
+{
+    const dim3 grid((unsigned)((q.cols + 127) / 128), (unsigned)((q.rows + 127) / 128));
+    if (q.cout.fmt == MXQ_FMT_E2M3)
+        hipLaunchKernelGGL((k_quant_dual16<GRID, ROUND, HN, FR, MXQ_FMT_E2M3>), grid, dim3(256), 0,
+                           q.s, q.x, q.rows, q.cols, q.ld, q.rout, q.cout, q.vec, q.kn);
+    else
+        hipLaunchKernelGGL((k_quant_dual16<GRID, ROUND, HN, FR, MXQ_FMT_FP4>), grid, dim3(256), 0,
+                           q.s, q.x, q.rows, q.cols, q.ld, q.rout, q.cout, q.vec, q.kn);
+}
+
+template <int GRID, int ROUND, int HN>
+void launch_dual_fmt(const DualLaunch &q)
+{
+    if (q.rout.fmt == MXQ_FMT_E2M3)
+        launch_dual_fc<GRID, ROUND, HN, MXQ_FMT_E2M3>(q);
+    else
+        launch_dual_fc<GRID, ROUND, HN, MXQ_FMT_FP4>(q);
+}
+
+template <int GRID, int ROUND>
+void launch_dual_hn(int hn, const DualLaunch &q)
+{
+    switch (hn) {
+    case 0: launch_dual_fmt<GRID, ROUND, 0>(q); break;
+    case 16: launch_dual_fmt<GRID, ROUND, 16>(q); break;
+    default: launch_dual_fmt<GRID, ROUND, 32>(q); break;
+    }
+}
 
 template <int GRID, int ROUND, int HN>
 void launch_row16_fmt(const RowLaunch &q)
@@ -511,6 +757,15 @@ void launch_col_hn(int hn, const ColLaunch &q)
 }
 
 }  // namespace
+
+hipError_t launch_quant_dual16(int grid, int round, int hn, const DualLaunch &q)
+{
+    if (grid == kE2M1)
+        round == kRTNE ? launch_dual_hn<kE2M1, kRTNE>(hn, q) : launch_dual_hn<kE2M1, kSR>(hn, q);
+    else
+        round == kRTNE ? launch_dual_hn<kE1M2, kRTNE>(hn, q) : launch_dual_hn<kE1M2, kSR>(hn, q);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_row16(int grid, int round, int hn, const RowLaunch &q)
 {
