@@ -151,6 +151,8 @@ def parse():
                     help="skip the bias / SQNR diagnostics")
     ap.add_argument("--no-fusion", action="store_true",
                     help="skip the fused / standalone / unfused quantize comparison")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the device-copy rate and the vendor-library GEMM reference")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -308,6 +310,9 @@ def main():
     if not args.no_fusion:
         rec["fusion"] = fusion_ratios(torch, mxq, synth, dev, max(args.steps, 10))
 
+    if not args.no_context:
+        rec["context"] = context_report(torch, dev, kernels)
+
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -322,6 +327,61 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, args.cpu_seconds)
 
     print(json.dumps(rec), flush=True)
+
+
+def context_report(torch, dev, kernels):
+    """What this GPU delivers outside this library, measured after the timed
+    region: a plain 1 GiB device-to-device copy (the practical HBM rate; each
+    quantizer's rate is also given as a fraction of it), and the vendor's own
+    block-scaled FP4 GEMM (hipBLASLt through torch._scaled_mm, E2M1 operands
+    with E8M0 scales per 32, bf16 output) at the weight-gradient shape, for
+    comparison with this library's GEMM (fp32 output)."""
+    ctx = {}
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    ctx["device_copy_GBps"] = round(copy_gbs, 1)
+    ctx["quantize_frac_of_copy"] = {k: round(v["achieved"] / copy_gbs, 4)
+                                    for k, v in kernels.items() if v["unit"] == "GB/s"}
+    del a, b
+    try:
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+        qa = torch.randint(0, 256, (N, T // 2), dtype=torch.uint8, device=dev, generator=g)
+        qb = torch.randint(0, 256, (K, T // 2), dtype=torch.uint8, device=dev, generator=g)
+        sa = torch.randint(124, 131, (N, T // 32), dtype=torch.uint8, device=dev, generator=g)
+        sb = torch.randint(124, 131, (K, T // 32), dtype=torch.uint8, device=dev, generator=g)
+        fa, fb = qa.view(torch.float4_e2m1fn_x2), qb.view(torch.float4_e2m1fn_x2)
+        ea, eb = sa.view(torch.float8_e8m0fnu), sb.view(torch.float8_e8m0fnu)
+
+        def mm():
+            return torch._scaled_mm(fa, fb.t(), ea, eb, out_dtype=torch.bfloat16)
+        for _ in range(3):
+            mm()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            mm()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        ctx["vendor_fp4_gemm"] = {"library": "hipBLASLt via torch._scaled_mm", "out_dtype": "bf16",
+                                  "m": N, "n": K, "k": T, "avg_us": round(us, 2),
+                                  "TFLOP_s": round(2.0 * N * K * T / (us * 1e-6) / 1e12, 1)}
+    except Exception as ex:  # not every torch build has block-scaled FP4 products
+        ctx["vendor_fp4_gemm"] = {"unavailable": f"{type(ex).__name__}: {str(ex)[:160]}"}
+    torch.cuda.empty_cache()
+    return ctx
 
 
 def quality_report(torch, mxq, synth, dev):
