@@ -52,6 +52,11 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
 /* style grid with equal spacing.  Both are decoded here from their bit      */
 /* fields as small floats: E2M1 with exponent bias 1 (levels 0 .. 6) and     */
 /* E1M2 with exponent bias 0 (levels 0, 0.5, ..., 3.5).                      */
+/*                                                                           */
+/* [UFP4] "Resultados Experimentais" (ablations) also tries E2M1 with its    */
+/* range restricted, a cap on the largest value, as a stand-in for a uniform */
+/* grid.  Those grids keep E2M1's codes and values and stop at a top code:   */
+/* code 6 (value 4) or code 5 (value 3).                                     */
 /* ------------------------------------------------------------------------ */
 static double minifloat_value(int ebits, int mbits, int bias, int code)
 {
@@ -66,16 +71,29 @@ static double minifloat_value(int ebits, int mbits, int bias, int code)
 
 double orc_grid_level(int grid, int m)
 {
-    if (grid == ORC_GRID_E2M1)
-        return minifloat_value(2, 1, 1, m);
-    return minifloat_value(1, 2, 0, m);
+    if (grid == ORC_GRID_E1M2)
+        return minifloat_value(1, 2, 0, m);
+    return minifloat_value(2, 1, 1, m);      /* E2M1 and its capped forms */
 }
 
+int orc_grid_top(int grid)
+{
+    if (grid == ORC_GRID_E2M1_MAX4)
+        return 6;
+    if (grid == ORC_GRID_E2M1_MAX3)
+        return 5;
+    return 7;
+}
+
+/* The block maximum is mapped into the binade (2^emax, 2^(emax+1)] that     */
+/* holds the grid's top level: emax = ceil(log2(top)) - 1.  E2M1 (top 6)     */
+/* gives 2 and E1M2 (top 3.5) gives 1, the usual floor(log2(top)); a cap of  */
+/* 4 or 3 gives 1, so a capped E2M1 block spans [2, 4) before rounding.      */
 int orc_grid_emax(int grid)
 {
     int k;
-    frexp(orc_grid_level(grid, 7), &k);    /* top level = f * 2^k, f in [0.5,1) */
-    return k - 1;
+    double f = frexp(orc_grid_level(grid, orc_grid_top(grid)), &k);   /* top = f * 2^k */
+    return f == 0.5 ? k - 2 : k - 1;
 }
 
 /* ------------------------------------------------------------------------ */
@@ -159,7 +177,7 @@ int orc_round_rtne(int grid, double a)
     /* nearest level; on a tie between neighbours k-1 and k, the even code */
     int best = 0;
     double bestd = fabs(a - orc_grid_level(grid, 0));
-    for (int k = 1; k < 8; ++k) {
+    for (int k = 1; k <= orc_grid_top(grid); ++k) {
         double d = fabs(a - orc_grid_level(grid, k));
         if (d < bestd || (d == bestd && (k % 2) == 0)) {
             best = k;
@@ -171,10 +189,11 @@ int orc_round_rtne(int grid, double a)
 
 int orc_round_sr(int grid, double a, uint32_t r, int bits)
 {
-    if (a >= orc_grid_level(grid, 7))
-        return 7;                               /* top bin clamps */
+    const int top = orc_grid_top(grid);
+    if (a >= orc_grid_level(grid, top))
+        return top;                             /* top bin clamps */
     int k = 0;
-    while (k < 7 && orc_grid_level(grid, k + 1) <= a)
+    while (k < top && orc_grid_level(grid, k + 1) <= a)
         ++k;
     double lo = orc_grid_level(grid, k);
     if (a == lo)
@@ -421,7 +440,7 @@ int orc_stats(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axi
     int64_t k = axis == ORC_AXIS_ROW ? cols : rows;
     int64_t nblk = k / 32;
     int64_t bbytes = fmt == ORC_FMT_FP4 ? 16 : 24;
-    double top = orc_grid_level(p->grid, 7);
+    double top = orc_grid_level(p->grid, orc_grid_top(p->grid));
     for (int64_t line = 0; line < lines; ++line) {
         for (int64_t jb = 0; jb < nblk; ++jb) {
             int64_t b = line * nblk + jb;

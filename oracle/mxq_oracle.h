@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-enum { ORC_GRID_E2M1 = 0, ORC_GRID_E1M2 = 1 };
+enum { ORC_GRID_E2M1 = 0, ORC_GRID_E1M2 = 1, ORC_GRID_E2M1_MAX4 = 2, ORC_GRID_E2M1_MAX3 = 3 };
 enum { ORC_RTNE = 0, ORC_SR = 1 };
 enum { ORC_FMT_FP4 = 0, ORC_FMT_E2M3 = 1 };
 enum { ORC_AXIS_ROW = 0, ORC_AXIS_COL = 1 };
@@ -68,9 +68,13 @@ typedef struct {
 /* Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): out = bijection(ctr; key). */
 void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]);
 
-/* Grid level G_m (m = 0..7) decoded from the element format's bit fields. */
+/* Grid level G_m (m = 0..7) decoded from the element format's bit fields
+ * (the capped E2M1 grids decode their codes as E2M1). */
 double orc_grid_level(int grid, int m);
-/* Exponent of the grid's largest level (E2M1: 6 = 1.5*2^2 -> 2; E1M2: 3.5 -> 1). */
+/* Largest code the grid emits: 7, or 6 / 5 for E2M1 capped at 4 / 3. */
+int orc_grid_top(int grid);
+/* emax = ceil(log2(top level)) - 1: the block maximum is mapped into
+ * (2^emax, 2^(emax+1)]; E2M1 (top 6) -> 2, E1M2 (top 3.5) -> 1, caps 4 and 3 -> 1. */
 int orc_grid_emax(int grid);
 
 /* In-place unnormalized fp32 fast Walsh-Hadamard transform, Sylvester order,

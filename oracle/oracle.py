@@ -15,7 +15,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(HERE, "libmxq_oracle.so")
 
-GRID_E2M1, GRID_E1M2 = 0, 1
+GRID_E2M1, GRID_E1M2, GRID_E2M1_MAX4, GRID_E2M1_MAX3 = 0, 1, 2, 3
 RTNE, SR = 0, 1
 FMT_FP4, FMT_E2M3 = 0, 1
 AXIS_ROW, AXIS_COL = 0, 1
@@ -71,6 +71,7 @@ def lib():
         L.orc_grid_level.argtypes = [C.c_int, C.c_int]
         L.orc_grid_level.restype = C.c_double
         L.orc_grid_emax.argtypes = [C.c_int]
+        L.orc_grid_top.argtypes = [C.c_int]
         L.orc_fwht_f32.argtypes = [P, C.c_int]
         L.orc_rotate_block.argtypes = [P, C.c_int, C.c_uint32, P]
         L.orc_scale_code.argtypes = [C.c_int, P]
@@ -119,6 +120,11 @@ def grid_levels(grid: int) -> list[float]:
 
 def grid_emax(grid: int) -> int:
     return lib().orc_grid_emax(grid)
+
+
+def grid_top(grid: int) -> int:
+    """Largest code m the grid emits (7; 6 and 5 for E2M1 capped at 4 and 3)."""
+    return lib().orc_grid_top(grid)
 
 
 def fwht_f32(u: np.ndarray) -> np.ndarray:

@@ -8,6 +8,7 @@ import numpy as np
 import pytest
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
+GRID_NAMES = {"e2m1": 0, "e1m2": 1, "e2m1max4": 2, "e2m1max3": 3}
 
 
 def _rows(name):
@@ -19,8 +20,7 @@ def _rows(name):
 
 def test_rtne_tie_table(orc):
     for grid, a, code in _rows("rtne_ties.txt"):
-        g = 0 if grid == "e2m1" else 1
-        assert orc.round_rtne(g, float(a)) == int(code), (grid, a)
+        assert orc.round_rtne(GRID_NAMES[grid], float(a)) == int(code), (grid, a)
 
 
 def _numpy_rtne(grid: int, a: np.ndarray) -> np.ndarray:
@@ -29,19 +29,23 @@ def _numpy_rtne(grid: int, a: np.ndarray) -> np.ndarray:
     a = a.astype(np.float64)
     if grid == 1:
         return np.minimum(np.round(2 * a), 7).astype(np.int64)
+    if grid in (2, 3):
+        # E2M1 capped at 4 / 3: nearest of the levels up to the cap, i.e. the
+        # E2M1 rounding with every code above the cap brought down to it
+        return np.minimum(_numpy_rtne(0, a), 6 if grid == 2 else 5)
     lo = np.round(2 * a)                     # [0, 2): step 0.5, codes 0..4
     mid = np.round(a) + 2                    # [2, 4): step 1, codes 4..6
     hi = np.minimum(np.round(a / 2) + 4, 7)  # [4, inf): step 2, codes 6, 7
     return np.where(a < 2, lo, np.where(a < 4, mid, hi)).astype(np.int64)
 
 
-@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("grid", [0, 1, 2, 3])
 def test_rtne_exhaustive_bf16_magnitudes(orc, grid):
     # every non-negative finite bf16 value, shifted into the normalized range
     # [0, 2^(emax+1)) by a power of two, as the scale would
     bits = np.arange(0, 0x7F80, dtype=np.uint32)
     vals = (bits << 16).view(np.float32).astype(np.float64)
-    top = 8.0 if grid == 0 else 4.0
+    top = 8.0 if grid == 0 else 4.0             # 2^(emax+1)
     # fold each value into [0, top) by its own power of two (keeps all
     # mantissa patterns), plus the raw tiny values
     with np.errstate(divide="ignore"):
@@ -53,20 +57,22 @@ def test_rtne_exhaustive_bf16_magnitudes(orc, grid):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("grid", [0, 1, 2, 3])
 def test_rtne_invariants(orc, grid):
-    lv = np.array(orc.grid_levels(grid))
+    T = orc.grid_top(grid)
+    lv = np.array(orc.grid_levels(grid))[:T + 1]
     g = np.random.Generator(np.random.PCG64(1))
-    a = np.sort(g.uniform(0, 2 * lv[7], 20000))
+    a = np.sort(g.uniform(0, 2 * lv[T], 20000))
     m = np.array([orc.round_rtne(grid, x) for x in a])
     assert np.all(np.diff(m) >= 0)                       # monotone
-    inside = a <= lv[7]
+    assert m.max() == T                                  # never above the top code
+    inside = a <= lv[T]
     gaps = np.diff(lv)
     # nearest: never more than half the local gap away
     k = np.searchsorted(lv, a[inside], side="right") - 1
-    k = np.clip(k, 0, 6)
+    k = np.clip(k, 0, T - 1)
     assert np.all(np.abs(lv[m[inside]] - a[inside]) <= gaps[k] / 2 + 1e-15)
-    assert np.all(m[~inside] == 7)                       # saturates
+    assert np.all(m[~inside] == T)                       # saturates
 
 
 def _sr_expect(orc, grid, a, bits):
@@ -77,35 +83,37 @@ def _sr_expect(orc, grid, a, bits):
     return tot / (1 << bits)
 
 
-@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("grid", [0, 1, 2, 3])
 def test_sr_exact_expectation_all_random_values(orc, grid):
-    lv = orc.grid_levels(grid)
+    T = orc.grid_top(grid)
+    lv = orc.grid_levels(grid)[:T + 1]
     g = np.random.Generator(np.random.PCG64(7 + grid))
-    pts = list(g.uniform(0, lv[7], 6)) + [0.1, 0.3, lv[3], (lv[5] + lv[6]) / 2]
+    pts = list(g.uniform(0, lv[T], 6)) + [0.1, 0.3, lv[3], (lv[T - 2] + lv[T - 1]) / 2]
     for a in pts:
         for bits in (8, 16):
             if bits == 16 and a not in pts[:3]:
                 continue  # keep the 2^16 enumeration to a few points
-            k = max(i for i in range(8) if lv[i] <= a)
-            gap = lv[k + 1] - lv[k] if k < 7 else 0.0
+            k = max(i for i in range(T + 1) if lv[i] <= a)
+            gap = lv[k + 1] - lv[k] if k < T else 0.0
             e = _sr_expect(orc, grid, a, bits)
             # unbiased up to the resolution of B random bits
             assert abs(e - a) <= gap * 2.0 ** -(bits + 1) + 1e-15, (a, bits)
 
 
 def test_sr_neighbours_only_and_top_clamp(orc):
-    for grid in (0, 1):
-        lv = orc.grid_levels(grid)
+    for grid in (0, 1, 2, 3):
+        T = orc.grid_top(grid)
+        lv = orc.grid_levels(grid)[:T + 1]
         g = np.random.Generator(np.random.PCG64(3))
-        for a in g.uniform(0, lv[7], 200):
-            k = max(i for i in range(8) if lv[i] <= a)
+        for a in g.uniform(0, lv[T], 200):
+            k = max(i for i in range(T + 1) if lv[i] <= a)
             for r in (0, 1, 777, 32767, 65535):
                 m = orc.round_sr(grid, a, r, 16)
-                assert m in (k, min(k + 1, 7))
+                assert m in (k, min(k + 1, T))
         top = 2.0 ** (orc.grid_emax(grid) + 1)
-        for a in np.linspace(lv[7], top, 9)[:-1]:
-            assert all(orc.round_sr(grid, a, r, 16) == 7 for r in (0, 65535))
-        for m in range(8):                       # exact levels stay put
+        for a in np.linspace(lv[T], max(top, lv[T] + 1), 9)[:-1]:
+            assert all(orc.round_sr(grid, a, r, 16) == T for r in (0, 65535))
+        for m in range(T + 1):                   # exact levels stay put
             assert orc.round_sr(grid, lv[m], 0, 16) == m
 
 
@@ -121,7 +129,7 @@ def test_sr_round_up_count_closed_form(orc):
 
 
 def _bias_rows():
-    return [(0 if g == "e2m1" else 1, int(c), float(lo), float(hi), float(b))
+    return [(GRID_NAMES[g], int(c), float(lo), float(hi), float(b))
             for g, c, lo, hi, b in _rows("shrinkage_bias.txt")]
 
 

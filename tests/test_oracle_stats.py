@@ -57,7 +57,7 @@ def test_stats_on_grid_data_has_zero_error(orc):
         assert st["level_count"] == np.bincount(m.reshape(-1), minlength=8).tolist()
 
 
-@pytest.mark.parametrize("grid", [0, 1])
+@pytest.mark.parametrize("grid", [0, 1, 2, 3])
 def test_per_level_bias_matches_closed_form_on_locally_uniform_data(orc, grid):
     # each block pins its scale with one element just below 2^(emax+1)*2^e
     # (exact in bf16);
@@ -67,7 +67,7 @@ def test_per_level_bias_matches_closed_form_on_locally_uniform_data(orc, grid):
     for line in open(os.path.join(GOLD, "shrinkage_bias.txt")):
         if line.strip() and not line.startswith("#"):
             g_, c, lo, hi, b = line.split()
-            if (g_ == "e2m1") == (grid == 0):
+            if {"e2m1": 0, "e1m2": 1, "e2m1max4": 2, "e2m1max3": 3}[g_] == grid:
                 rows.append((int(c), float(b)))
     top = 8.0 if grid == 0 else 4.0
     g = np.random.Generator(np.random.PCG64(77 + grid))
@@ -84,9 +84,9 @@ def test_per_level_bias_matches_closed_form_on_locally_uniform_data(orc, grid):
     for code, bias in rows:
         cnt = st["level_count"][code]
         tot = st["level_err_norm"][code]
-        if code == 7:                            # remove the n pinning elements
+        if code == orc.grid_top(grid):           # remove the n pinning elements
             cnt -= n
-            tot -= n * (lv[7] - float(pin))
+            tot -= n * (lv[code] - float(pin))
         mean = tot / cnt
         # bf16 rounding of the inputs perturbs a by <= 2^-8 relative
         assert abs(mean - bias) < 0.02 + 4 * 0.3 / np.sqrt(cnt), (code, mean, bias)
