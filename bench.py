@@ -404,10 +404,11 @@ def quality_report(torch, mxq, synth, dev):
     def to_dev(a):
         return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
 
-    def summarize(st):
+    def summarize(st, grid):
         n, ns = st["n"], st["n_saturated"]
         lc = [int(v) for v in st["level_count"]]
         return {"delta_rel": st["sum_signed_err"] / st["sum_abs_y"],
+                "bucket_ratio": mxq.bucket_ratio(lc, grid),
                 "delta_norm": st["sum_err_norm"] / n,
                 "sqnr_db": 10.0 * math.log10(st["sum_y2"] / st["sum_err2"]),
                 "saturated_frac": ns / n,
@@ -420,28 +421,30 @@ def quality_report(torch, mxq, synth, dev):
         key = "row" if axis == 0 else "col"
         return mxq.bias_stats(x, axis, q[key][0], q[key][1], 0, **kn)
 
-    grids = {"e2m1": mxq.GRID_E2M1, "e1m2": mxq.GRID_E1M2}
+    grids = {"e2m1": mxq.GRID_E2M1, "e1m2": mxq.GRID_E1M2, "e2m1_max4": mxq.GRID_E2M1_MAX4,
+             "e2m1_max3": mxq.GRID_E2M1_MAX3}
     rep = {}
     x1 = to_dev(synth.x_1024())
-    rep["x_1024_row_n0"] = {g: summarize(stats(x1, 0, grid=v)) for g, v in grids.items()}
+    rep["x_1024_row_n0"] = {g: summarize(stats(x1, 0, grid=v), v) for g, v in grids.items()}
     x2 = to_dev(synth.x_8192x4096())
     r2 = {}
     for g, v in grids.items():
-        a = summarize(stats(x2, 0, grid=v))
-        b = summarize(stats(x2, 0, grid=v, hadamard_n=16))
-        r2[g] = {"n0": a, "h16": b, "delta_sqnr_db": b["sqnr_db"] - a["sqnr_db"]}
+        a = summarize(stats(x2, 0, grid=v), v)
+        b = summarize(stats(x2, 0, grid=v, hadamard_n=16), v)
+        r2[g] = {"n0": a, "h16": b, "delta_sqnr_db": b["sqnr_db"] - a["sqnr_db"],
+                 "delta_bucket_ratio": b["bucket_ratio"] - a["bucket_ratio"]}
     rep["x_8192x4096_row"] = r2
     del x1, x2
     w = to_dev(synth.w_14336x4096())
     ws = synth.sign_mask(synth.SIGNS_W, 32)
     rep["w_14336x4096_h32_signs"] = {
-        g: {"row": summarize(stats(w, 0, grid=v, hadamard_n=32, sign_mask=ws)),
-            "col": summarize(stats(w, 1, grid=v, hadamard_n=32, sign_mask=ws))}
+        g: {"row": summarize(stats(w, 0, grid=v, hadamard_n=32, sign_mask=ws), v),
+            "col": summarize(stats(w, 1, grid=v, hadamard_n=32, sign_mask=ws), v)}
         for g, v in grids.items()}
     del w
     dy = to_dev(synth.dy_16384x4096())
     ds = synth.sign_mask(synth.SIGNS_DY, 16)
-    r4 = {g: summarize(stats(dy, 1, grid=v, hadamard_n=16, sign_mask=ds)) for g, v in grids.items()}
+    r4 = {g: summarize(stats(dy, 1, grid=v, hadamard_n=16, sign_mask=ds), v) for g, v in grids.items()}
     tot = tot_sat = 0.0
     n_unsat = n_sat = 0
     for seed in range(64):
@@ -462,7 +465,9 @@ def quality_report(torch, mxq, synth, dev):
     ref = dyw.double().t().contiguous() @ xw.double()
     sg = synth.sign_mask(synth.SIGNS_WGRAD, 16)
     r5 = {}
-    for name, g, f in (("e1m2_e2m3", mxq.GRID_E1M2, mxq.FMT_E2M3), ("e2m1_fp4", mxq.GRID_E2M1, mxq.FMT_FP4)):
+    for name, g, f in (("e1m2_e2m3", mxq.GRID_E1M2, mxq.FMT_E2M3), ("e2m1_fp4", mxq.GRID_E2M1, mxq.FMT_FP4),
+                       ("e2m1_max4_fp4", mxq.GRID_E2M1_MAX4, mxq.FMT_FP4),
+                       ("e2m1_max3_fp4", mxq.GRID_E2M1_MAX3, mxq.FMT_FP4)):
         qd = mxq.quantize(dyw, grid=g, round=mxq.SR, hadamard_n=16, sign_mask=sg,
                           sr_seed=synth.SR_SEED_WGRAD, row=False, col=True, col_fmt=f,
                           col_layout=mxq.LAYOUT_MFMA)["col"]

@@ -36,7 +36,7 @@ __device__ __forceinline__ uint32_t nibble_of_e2m3(int grid, uint32_t c)
 {
     const uint32_t s = (c >> 2) & 8u, mag = c & 31u;
     uint32_t m;
-    if (grid == MXQ_GRID_E2M1)
+    if (grid != MXQ_GRID_E1M2)
         m = mag >> 2;
     else
         m = mag < 16u ? (mag >> 2) : ((mag - 8u) >> 1);
@@ -152,7 +152,9 @@ __global__ __launch_bounds__(256) void k_stats(const uint16_t *__restrict__ x, i
     const int64_t nbk = k / 32;
     const uint64_t nblocks = (uint64_t)(lines * nbk);
     const uint32_t sg = HN ? (kn.sign_mask >> ((8 * pos) % (HN ? HN : 32))) & 0xFFu : 0u;
-    const float top = grid == MXQ_GRID_E2M1 ? 6.0f : 3.5f;
+    const float top = grid == MXQ_GRID_E2M1 ? 6.0f
+                      : grid == MXQ_GRID_E1M2 ? 3.5f
+                      : grid == MXQ_GRID_E2M1_MAX4 ? 4.0f : 3.0f;
     const int emax = grid == MXQ_GRID_E2M1 ? 2 : 1;
 
     StatAcc acc;
@@ -297,7 +299,7 @@ extern "C" mxq_status mxq_dequantize(const mxq_qtensor *q, int64_t lines, int64_
         return MXQ_ERR_NULL;
     if (q->fmt != MXQ_FMT_FP4 && q->fmt != MXQ_FMT_E2M3)
         return MXQ_ERR_UNSUPPORTED;
-    if (q->grid != MXQ_GRID_E2M1 && q->grid != MXQ_GRID_E1M2)
+    if (q->grid < MXQ_GRID_E2M1 || q->grid > MXQ_GRID_E2M1_MAX3)
         return MXQ_ERR_UNSUPPORTED;
     if (out_dtype != MXQ_OUT_F32 && out_dtype != MXQ_OUT_BF16)
         return MXQ_ERR_UNSUPPORTED;

@@ -32,6 +32,8 @@ struct QKnobs {
     uint32_t seed_lo, seed_hi;
     uint32_t stream;
     uint32_t sr_bits;  // 8 or 16
+    int32_t emax;      // E2M1 family: 2, or 1 with a cap (E1M2 kernels use 1)
+    float top2;        // E2M1 family: twice the top level (12, or 8 / 6 with a cap)
 };
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
@@ -210,22 +212,29 @@ __device__ __forceinline__ void rotate16_raw(float (&v)[16], int pos)
 // ---- rounding of 8 signed values y * inv onto the grid --------------------
 // Returns the sign-magnitude nibbles, element i in bits 4i..4i+3.  `r` and
 // `tpb` = 2^(B+1) are only read for SR.
+// `top` is the E2M1 family's top level (6, or the cap 4 / 3): larger
+// magnitudes are brought down to it first.
 template <int GRID, int ROUND>
 __device__ __forceinline__ uint32_t round8(const float (&v)[8], float inv, const uint32_t (&r)[8],
-                                           float tpb)
+                                           float tpb, float top)
 {
     uint32_t w = 0;
+    const bool capped = GRID == kE2M1 && top < 6.0f;
     if constexpr (GRID == kE2M1 && ROUND == kRTNE) {
         // the gfx950 FP4 convert rounds to nearest-even E2M1 with saturation
         // and keeps the sign (including -0); y * 2^-e is exact
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * inv, v[1] * inv, 1.0f, 0);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * inv, v[3] * inv, 1.0f, 1);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * inv, v[5] * inv, 1.0f, 2);
-        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * inv, v[7] * inv, 1.0f, 3);
+        float s[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            s[i] = capped ? __builtin_amdgcn_fmed3f(v[i] * inv, -top, top) : v[i] * inv;
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[0], s[1], 1.0f, 0);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[2], s[3], 1.0f, 1);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[4], s[5], 1.0f, 2);
+        w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, s[6], s[7], 1.0f, 3);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const float a = fabsf(v[i]) * inv;
+            const float a = capped ? fminf(fabsf(v[i]) * inv, top) : fabsf(v[i]) * inv;
             uint32_t m;
             if constexpr (ROUND == kRTNE)
                 m = GRID == kE1M2 ? rtne_e1m2(a) : rtne_e2m1_soft(a);

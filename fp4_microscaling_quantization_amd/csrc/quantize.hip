@@ -16,7 +16,8 @@ namespace mxq {
 template <int GRID, int ROUND>
 __global__ __launch_bounds__(256) void k_round_to_grid(const float *__restrict__ a,
                                                        const uint16_t *__restrict__ rnd, int64_t n,
-                                                       int sr_bits, uint8_t *__restrict__ out)
+                                                       int sr_bits, float top,
+                                                       uint8_t *__restrict__ out)
 {
     const int64_t i0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
     if (i0 >= n)
@@ -28,7 +29,7 @@ __global__ __launch_bounds__(256) void k_round_to_grid(const float *__restrict__
         v[k] = (i0 + k < n) ? a[i0 + k] : 0.0f;
         r[k] = (ROUND == kSR && i0 + k < n) ? (uint32_t)rnd[i0 + k] : 0u;
     }
-    const uint32_t w = round8<GRID, ROUND>(v, 1.0f, r, sr_bits == 16 ? 131072.0f : 512.0f);
+    const uint32_t w = round8<GRID, ROUND>(v, 1.0f, r, sr_bits == 16 ? 131072.0f : 512.0f, top);
 #pragma unroll
     for (int k = 0; k < 8; ++k)
         if (i0 + k < n)
@@ -41,7 +42,7 @@ mxq_status check_qconfig(const mxq_qconfig *cfg)
 {
     if (!cfg)
         return MXQ_ERR_NULL;
-    if (cfg->grid != MXQ_GRID_E2M1 && cfg->grid != MXQ_GRID_E1M2)
+    if (cfg->grid < MXQ_GRID_E2M1 || cfg->grid > MXQ_GRID_E2M1_MAX3)
         return MXQ_ERR_UNSUPPORTED;
     if (cfg->round != MXQ_ROUND_RTNE && cfg->round != MXQ_ROUND_SR)
         return MXQ_ERR_UNSUPPORTED;
@@ -79,6 +80,10 @@ QKnobs make_knobs(const mxq_qconfig *cfg)
     kn.seed_hi = (uint32_t)(cfg->sr_seed >> 32);
     kn.stream = cfg->sr_stream;
     kn.sr_bits = cfg->sr_bits == 8 ? 8u : 16u;
+    // the E2M1 family's scale exponent and (twice) its top level; the capped
+    // grids map the block maximum into [2, 4) and stop at 4 or 3
+    kn.emax = cfg->grid == MXQ_GRID_E2M1 ? 2 : 1;
+    kn.top2 = cfg->grid == MXQ_GRID_E2M1_MAX4 ? 8.0f : cfg->grid == MXQ_GRID_E2M1_MAX3 ? 6.0f : 12.0f;
     return kn;
 }
 
@@ -125,22 +130,25 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
     const QKnobs kn = make_knobs(cfg);
     hipStream_t s = static_cast<hipStream_t>(stream);
 
+    // kernels come in two grid families: E1M2, and E2M1 with or without a cap
+    // (the cap and the scale exponent travel in the knobs)
+    const int fam = cfg->grid == MXQ_GRID_E1M2 ? kE1M2 : kE2M1;
     hipError_t e;
     if (!col_out) {
         // blocks along the contiguous dimension: 16-byte loads when aligned
         const uint64_t nbr = (uint64_t)cols / 32;
         RowLaunch r{xx, (uint64_t)rows * nbr, (uint32_t)nbr, ld_x, ld_x == cols ? 1 : 0,
                     (xa % 16 == 0 && ld_x % 8 == 0) ? 1 : 0, rout, kn, s};
-        e = launch_quant_row16(cfg->grid, cfg->round, cfg->hadamard_n, r);
+        e = launch_quant_row16(fam, cfg->round, cfg->hadamard_n, r);
     } else {
         // blocks along rows (alone or with the row output): 8-byte loads when aligned
         const int vec8 = (xa % 8 == 0 && ld_x % 4 == 0) ? 1 : 0;
         if (!row_out) {
             ColLaunch c{xx, rows, cols, ld_x, cout, vec8, kn, s};
-            e = launch_quant_col(cfg->grid, cfg->round, cfg->hadamard_n, c);
+            e = launch_quant_col(fam, cfg->round, cfg->hadamard_n, c);
         } else {
             DualLaunch d{xx, rows, cols, ld_x, rout, cout, vec8, kn, s};
-            e = launch_quant_dual16(cfg->grid, cfg->round, cfg->hadamard_n, d);
+            e = launch_quant_dual16(fam, cfg->round, cfg->hadamard_n, d);
         }
     }
     return e == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
@@ -150,7 +158,7 @@ extern "C" mxq_status mxq_round_to_grid(int32_t grid, int32_t round, int32_t sr_
                                         const float *a, const uint16_t *rand, int64_t n,
                                         uint8_t *codes, void *stream)
 {
-    if ((grid != MXQ_GRID_E2M1 && grid != MXQ_GRID_E1M2) ||
+    if (grid < MXQ_GRID_E2M1 || grid > MXQ_GRID_E2M1_MAX3 ||
         (round != MXQ_ROUND_RTNE && round != MXQ_ROUND_SR) ||
         (round == MXQ_ROUND_SR && sr_bits != 8 && sr_bits != 16))
         return MXQ_ERR_UNSUPPORTED;
@@ -163,16 +171,18 @@ extern "C" mxq_status mxq_round_to_grid(int32_t grid, int32_t round, int32_t sr_
     const int64_t threads = (n + 7) / 8;
     const dim3 g((unsigned)((threads + 255) / 256));
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (grid == MXQ_GRID_E2M1) {
+    // top level of the E2M1 family: 6, or the cap
+    const float top = grid == MXQ_GRID_E2M1_MAX4 ? 4.0f : grid == MXQ_GRID_E2M1_MAX3 ? 3.0f : 6.0f;
+    if (grid != MXQ_GRID_E1M2) {
         if (round == MXQ_ROUND_RTNE)
-            hipLaunchKernelGGL((k_round_to_grid<kE2M1, kRTNE>), g, dim3(256), 0, s, a, rand, n, sr_bits, codes);
+            hipLaunchKernelGGL((k_round_to_grid<kE2M1, kRTNE>), g, dim3(256), 0, s, a, rand, n, sr_bits, top, codes);
         else
-            hipLaunchKernelGGL((k_round_to_grid<kE2M1, kSR>), g, dim3(256), 0, s, a, rand, n, sr_bits, codes);
+            hipLaunchKernelGGL((k_round_to_grid<kE2M1, kSR>), g, dim3(256), 0, s, a, rand, n, sr_bits, top, codes);
     } else {
         if (round == MXQ_ROUND_RTNE)
-            hipLaunchKernelGGL((k_round_to_grid<kE1M2, kRTNE>), g, dim3(256), 0, s, a, rand, n, sr_bits, codes);
+            hipLaunchKernelGGL((k_round_to_grid<kE1M2, kRTNE>), g, dim3(256), 0, s, a, rand, n, sr_bits, top, codes);
         else
-            hipLaunchKernelGGL((k_round_to_grid<kE1M2, kSR>), g, dim3(256), 0, s, a, rand, n, sr_bits, codes);
+            hipLaunchKernelGGL((k_round_to_grid<kE1M2, kSR>), g, dim3(256), 0, s, a, rand, n, sr_bits, top, codes);
     }
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
 }

@@ -100,7 +100,7 @@ template <int GRID, int ROUND, int HN, bool EXACT_LEVEL>
 __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk, const QKnobs &kn,
                                           float h, float h2)
 {
-    constexpr int EMAX = GRID == kE2M1 ? 2 : 1;
+    const int EMAX = GRID == kE2M1 ? kn.emax : 1;
     // ---- rotation: fp32 butterflies of stride 1, 2, 4, 8 in the lane, 16 across
     rotate16_raw<HN>(v, pos);
     if constexpr (HN == 32) {
@@ -165,11 +165,13 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
                 // levels 0.5 m: m = RNE(2a), saturated at 7
                 v[i] = rintf(__builtin_amdgcn_fmed3f(t, -7.0f, 7.0f));
             } else if constexpr (!EXACT_LEVEL) {
-                v[i] = t;  // the FP4 convert rounds t / 2 to nearest even, saturating at 6
+                // the FP4 convert rounds t / 2 to nearest even (saturating at 6);
+                // a capped grid stops at its cap first
+                v[i] = __builtin_amdgcn_fmed3f(t, -kn.top2, kn.top2);
             } else {
                 // E2M1 in software: round 2a to a multiple of 2 step by adding and
                 // subtracting 1.5 2^22 S (S = 2^max(floor(log2 2a), 1), whose ulp is 2 step)
-                const float a2 = fminf(fabsf(t), 12.0f);
+                const float a2 = fminf(fabsf(t), kn.top2);
                 const float S = as_f(max(as_u(a2) & 0x7F800000u, 0x40000000u));
                 const float G = S * 6291456.0f;
                 v[i] = copysignf((a2 + G) - G, t);
@@ -186,7 +188,7 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
                 v[i] = copysignf(ceilf(__builtin_fmaf(rf[i], -h2, x)), v[i]);
             } else {
                 // a in units of the local step (S / 4 for 2a below 2 S): x = 2a * 2 / S
-                const float a2 = fminf(fabsf(v[i]) * m2, 12.0f);
+                const float a2 = fminf(fabsf(v[i]) * m2, kn.top2);
                 const float S = as_f(max(as_u(a2) & 0x7F800000u, 0x40000000u));
                 const float x = __builtin_fmaf(a2, as_f(0x7F800000u - as_u(S)), -h);
                 v[i] = copysignf(ceilf(__builtin_fmaf(rf[i], -h2, x)) * S, v[i]);

@@ -520,8 +520,8 @@ int mfma_format(const mxq_qtensor *q)
 {
     if (q->fmt == MXQ_FMT_E2M3)
         return kMfmaFP6;
-    if (q->fmt == MXQ_FMT_FP4 && q->grid == MXQ_GRID_E2M1)
-        return kMfmaFP4;
+    if (q->fmt == MXQ_FMT_FP4 && q->grid != MXQ_GRID_E1M2)
+        return kMfmaFP4;   // E2M1 nibbles, capped or not
     return -1;  // E1M2 nibbles have no matrix-core type; use the E2M3 form
 }
 }  // namespace

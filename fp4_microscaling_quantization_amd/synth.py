@@ -14,7 +14,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-GRID_E2M1, GRID_E1M2 = 0, 1
+GRID_E2M1, GRID_E1M2, GRID_E2M1_MAX4, GRID_E2M1_MAX3 = 0, 1, 2, 3
 RTNE, SR = 0, 1
 FMT_FP4, FMT_E2M3 = 0, 1
 

@@ -54,9 +54,20 @@ typedef int32_t mxq_status;
 
 /* Element grids (the 3-bit magnitude m of a sign-magnitude nibble s<<3|m):
  *   MXQ_GRID_E2M1: m -> {0, 0.5, 1, 1.5, 2, 3, 4, 6}; top-level exponent emax 2.
- *   MXQ_GRID_E1M2: m -> 0.5*m = {0, 0.5, ..., 3.5} (uniform); emax 1. */
+ *   MXQ_GRID_E1M2: m -> 0.5*m = {0, 0.5, ..., 3.5} (uniform); emax 1.
+ *   MXQ_GRID_E2M1_MAX4, MXQ_GRID_E2M1_MAX3: E2M1 with its range restricted,
+ *     the ablation of the gist.science summary "Repensando o Vies de
+ *     Encolhimento ... em FP4", "Resultados Experimentais": E2M1's codes and
+ *     values up to a cap of 4 (m <= 6) or 3 (m <= 5); larger magnitudes go to
+ *     the cap.  emax 1 for both, so a block's normalized maximum lies in
+ *     [2, 4).  Their codes are plain E2M1 nibbles (FP4 operands of the
+ *     matrix cores as they stand).
+ * In general emax = ceil(log2(top level)) - 1: the block maximum is mapped
+ * into the binade (2^emax, 2^(emax+1)] that holds the grid's top level. */
 #define MXQ_GRID_E2M1 0
 #define MXQ_GRID_E1M2 1
+#define MXQ_GRID_E2M1_MAX4 2
+#define MXQ_GRID_E2M1_MAX3 3
 
 /* Rounding of the normalized magnitude a = |y| / 2^e onto the grid:
  *   MXQ_ROUND_RTNE: nearest level, ties to the even code, saturating.

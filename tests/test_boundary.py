@@ -57,7 +57,7 @@ def test_quantize_validation(mxq_lib):
     assert q(None) == M.ERR_NULL
     assert q(good, x=None) == M.ERR_NULL
     assert q(good, row=None, col=None) == M.ERR_NULL
-    assert q(M.qconfig(grid=2)) == M.ERR_UNSUPPORTED
+    assert q(M.qconfig(grid=4)) == M.ERR_UNSUPPORTED
     assert q(M.qconfig(round=5)) == M.ERR_UNSUPPORTED
     assert q(M.qconfig(hadamard_n=8)) == M.ERR_UNSUPPORTED
     assert q(M.qconfig(round=M.SR, sr_bits=12)) == M.ERR_UNSUPPORTED
@@ -118,7 +118,8 @@ def test_dequant_stats_round_validation(mxq_lib):
                             _fake(0x80000), ws - 8, None) == M.ERR_WORKSPACE
     assert L.mxq_bias_stats(C.byref(cfg), _fake(), 64, 64, 64, 3, C.byref(q), _fake(0x70000),
                             _fake(0x80000), ws, None) == M.ERR_UNSUPPORTED
-    assert L.mxq_round_to_grid(3, 0, 16, _fake(), None, 10, _fake(), None) == M.ERR_UNSUPPORTED
+    assert L.mxq_round_to_grid(4, 0, 16, _fake(), None, 10, _fake(), None) == M.ERR_UNSUPPORTED
+    assert L.mxq_round_to_grid(-1, 0, 16, _fake(), None, 10, _fake(), None) == M.ERR_UNSUPPORTED
     assert L.mxq_round_to_grid(0, 1, 16, _fake(), None, 10, _fake(), None) == M.ERR_NULL
     assert L.mxq_round_to_grid(0, 0, 16, _fake(), None, -1, _fake(), None) == M.ERR_SHAPE
 

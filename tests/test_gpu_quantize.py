@@ -12,11 +12,14 @@ from gpuhelp import dev, host, say, special_matrix, to_dev_bf16
 pytestmark = pytest.mark.gpu
 
 KNOBS = [(g, r, n) for g in (0, 1) for r in (0, 1) for n in (0, 16, 32)]
+# E2M1 with its range capped at 4 (grid 2) or 3 (grid 3)
+KNOBS_CAP = [(g, r, n) for g in (2, 3) for r in (0, 1) for n in (0, 16, 32)]
+GRID_ID = {0: "e2m1", 1: "e1m2", 2: "e2m1max4", 3: "e2m1max3"}
 
 
 def _knob_id(k):
     g, r, n = k
-    return f"{'e2m1' if g == 0 else 'e1m2'}-{'rtne' if r == 0 else 'sr'}-h{n}"
+    return f"{GRID_ID[g]}-{'rtne' if r == 0 else 'sr'}-h{n}"
 
 
 def _params(orc, grid, rnd, n, seed=0, sr_bits=16):
@@ -75,7 +78,22 @@ def test_dual_parity(orc, shape, knobs):
     _check(orc, x, _params(orc, *knobs, seed=6), row_fmt=1, col_fmt=0, tag="dual")
 
 
-@pytest.mark.parametrize("knobs", KNOBS, ids=_knob_id)
+@pytest.mark.parametrize("shape", [(96, 160), (256, 256), (33, 4128)])
+@pytest.mark.parametrize("knobs", KNOBS_CAP, ids=_knob_id)
+def test_capped_e2m1_parity(orc, shape, knobs):
+    # every kernel (row, column, both) and both storage formats; data with
+    # outliers so blocks span the whole capped range
+    rows, cols = shape
+    x = synth.normal_outlier_channels(rows, cols, seed=rows, ch_seed=cols, frac=0.02)
+    for fmt in (0, 1):
+        _check(orc, x, _params(orc, *knobs, seed=rows), row_fmt=fmt, tag="cap-row")
+        if rows % 32 == 0:
+            _check(orc, x, _params(orc, *knobs, seed=cols), col_fmt=fmt, tag="cap-col")
+            _check(orc, x, _params(orc, *knobs, seed=7), row_fmt=fmt, col_fmt=1 - fmt,
+                   tag="cap-dual")
+
+
+@pytest.mark.parametrize("knobs", KNOBS + KNOBS_CAP, ids=_knob_id)
 def test_special_values(orc, knobs):
     x = special_matrix(96, 160, seed=11)
     p = _params(orc, *knobs, seed=9)

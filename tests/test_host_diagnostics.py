@@ -1,0 +1,39 @@
+"""CPU checks of the host-side diagnostics of the Python binding (no GPU):
+the effective bucket ratio exp(H)/L against its closed forms."""
+import math
+
+import numpy as np
+import pytest
+
+
+def test_bucket_ratio_closed_forms():
+    from fp4_microscaling_quantization_amd import mxq
+    # all levels equally used: exp(ln L) / L = 1
+    assert mxq.bucket_ratio([5] * 8, mxq.GRID_E2M1) == pytest.approx(1.0)
+    assert mxq.bucket_ratio([3] * 6 + [0, 0], mxq.GRID_E2M1_MAX3) == pytest.approx(1.0)
+    # one level only: 1 / L
+    assert mxq.bucket_ratio([9, 0, 0, 0, 0, 0, 0, 0], mxq.GRID_E1M2) == pytest.approx(1 / 8)
+    assert mxq.bucket_ratio([0, 0, 4, 0, 0, 0, 0, 0], mxq.GRID_E2M1_MAX4) == pytest.approx(1 / 7)
+    # k levels equally used: k / L
+    assert mxq.bucket_ratio([2, 2, 0, 0, 0, 0, 0, 0], mxq.GRID_E2M1) == pytest.approx(2 / 8)
+    # a skewed histogram: the entropy written out
+    c = [70, 20, 10, 0, 0, 0, 0, 0]
+    h = -(0.7 * math.log(0.7) + 0.2 * math.log(0.2) + 0.1 * math.log(0.1))
+    assert mxq.bucket_ratio(c, mxq.GRID_E2M1) == pytest.approx(math.exp(h) / 8)
+    assert math.isnan(mxq.bucket_ratio([0] * 8, mxq.GRID_E2M1))
+
+
+def test_bucket_ratio_rises_when_outliers_are_spread(orc):
+    # the oracle's level counts on outlier-channel data, without and with the
+    # H16 rotation: the rotation spreads each outlier over 16 positions, so
+    # fewer elements sit at level 0 and the ratio rises (for both grids)
+    from fp4_microscaling_quantization_amd import mxq, synth
+    x = synth.normal_outlier_channels(64, 512, seed=4, ch_seed=5, frac=0.02)
+    for grid in (mxq.GRID_E2M1, mxq.GRID_E1M2):
+        r = []
+        for n in (0, 16):
+            p = orc.qparams(grid=grid, hadamard_n=n)
+            codes, scales = orc.quantize(x, orc.AXIS_ROW, p)
+            st = orc.stats(x, orc.AXIS_ROW, p, codes, scales)
+            r.append(mxq.bucket_ratio(st["level_count"], grid))
+        assert 1 / 8 < r[0] < r[1] <= 1.0, r
