@@ -50,14 +50,14 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     "e1m2": {
-        "quantize_dy_col_sr": {"read": 67329524, "write": 26215086, "sha": "4a16a70551723b7c"},
-        "quantize_x_col_rtne": {"read": 67249526, "write": 26218094, "sha": "4a16a70551723b7c"},
-        "wgrad_gemm": {"read": 157553460, "write": 67112430, "sha": "48c98a6c76b266e1"},
+        "quantize_dy_col_sr": {"read": 67362489, "write": 26214830, "sha": "aea97bc8ac5ef34f"},
+        "quantize_x_col_rtne": {"read": 67270936, "write": 26218752, "sha": "aea97bc8ac5ef34f"},
+        "wgrad_gemm": {"read": 157553937, "write": 67116562, "sha": "89476f4b16a9b7b1"},
     },
     "e2m1": {
-        "quantize_dy_col_sr": {"read": 67370081, "write": 17825920, "sha": "4a16a70551723b7c"},
-        "quantize_x_col_rtne": {"read": 67235320, "write": 17829285, "sha": "4a16a70551723b7c"},
-        "wgrad_gemm": {"read": 107206916, "write": 67112896, "sha": "48c98a6c76b266e1"},
+        "quantize_dy_col_sr": {"read": 67387254, "write": 17826633, "sha": "aea97bc8ac5ef34f"},
+        "quantize_x_col_rtne": {"read": 67267743, "write": 17834779, "sha": "aea97bc8ac5ef34f"},
+        "wgrad_gemm": {"read": 107207982, "write": 67113216, "sha": "89476f4b16a9b7b1"},
     },
 }
 
