@@ -491,9 +491,12 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
 // bf16 words into an LDS image of the 128 x 128 tile.  After one barrier,
 // phase 2 reads the tile's rows back from LDS and runs the row kernel's work
 // on them (two lanes per row block, 16 consecutive columns each).  The LDS
-// row stride is 264 bytes: the two 16-row halves a wave writes at once then
-// fall 32 banks apart.
-constexpr int kTileRS = 264;   // LDS bytes per tile row (128 bf16 + 8 pad)
+// image has no padding (32 KiB, so with FP4 column codes four workgroups fit
+// in a CU); instead the 8-byte units of row r sit at unit ^ tile_swz(r).  The
+// two 16-row halves a wave writes at once then fall 32 banks apart, and the
+// 4 rows x 8 units of each 32-lane pass of a phase-2 read hit distinct banks.
+constexpr int kTileRS = 256;   // LDS bytes per tile row (128 bf16)
+__device__ __forceinline__ int tile_swz(int r) { return (r & 7) | (r & 16); }
 
 template <int GRID, int ROUND, int HN, int FMTR, int FMTC>
 __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict__ x, int64_t rows,
@@ -537,9 +540,11 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
             }
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-            *reinterpret_cast<uint2 *>(tile + (32 * wv + 16 * pos + i) * kTileRS + 8 * cg) =
+        for (int i = 0; i < 16; ++i) {
+            const int r = 32 * wv + 16 * pos + i;
+            *reinterpret_cast<uint2 *>(tile + r * kTileRS + 8 * (cg ^ tile_swz(r))) =
                 make_uint2(lo[i], hi[i]);
+        }
         if constexpr (HN > 0) {
             const uint32_t sg = HN == 16 ? kn.sign_mask : kn.sign_mask >> (16 * pos);
 #pragma unroll
@@ -622,10 +627,10 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
         rline[u] = (uint64_t)(row0 + lr);
         rjb[u] = (uint64_t)(col0 / 32 + lb);
         ok[u] = (int64_t)rline[u] < rows && rjb[u] < nbr;
-        const uint2 *src = reinterpret_cast<const uint2 *>(tile + lr * kTileRS + 64 * lb + 32 * pos);
+        const uint8_t *src = tile + lr * kTileRS;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint2 w = src[k];
+            const uint2 w = *reinterpret_cast<const uint2 *>(src + 8 * ((8 * lb + 4 * pos + k) ^ tile_swz(lr)));
             const uint32_t wd[2] = {w.x, w.y};
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
