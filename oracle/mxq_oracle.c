@@ -118,7 +118,7 @@ void orc_fwht_f32(float *u, int n)
     }
 }
 
-void orc_rotate_block(const float x[32], int n, uint32_t sign_mask, float y[32])
+void orc_rotate_block_signs(const float x[32], int n, uint32_t signs, float y[32])
 {
     if (n == 0) {
         for (int i = 0; i < 32; ++i)
@@ -130,12 +130,40 @@ void orc_rotate_block(const float x[32], int n, uint32_t sign_mask, float y[32])
         float u[32];
         for (int i = 0; i < n; ++i) {
             float v = x[s + i];
-            u[i] = ((sign_mask >> i) & 1u) ? -v : v;
+            u[i] = ((signs >> (s + i)) & 1u) ? -v : v;
         }
         orc_fwht_f32(u, n);
         for (int i = 0; i < n; ++i)
             y[s + i] = u[i] * c;
     }
+}
+
+/* one mask for every block: position i takes bit (i mod n) */
+static uint32_t mask_signs(int n, uint32_t mask)
+{
+    if (n == 16)
+        return (mask & 0xFFFFu) | ((mask & 0xFFFFu) << 16);
+    return n == 32 ? mask : 0u;
+}
+
+void orc_rotate_block(const float x[32], int n, uint32_t sign_mask, float y[32])
+{
+    orc_rotate_block_signs(x, n, mask_signs(n, sign_mask), y);
+}
+
+/* [NEWS] "Experimento de diagnostico": the signs are random; a sign vector as
+ * long as the quantization axis gives every block its own draw. */
+uint32_t orc_block_signs(const orc_qparams *p, uint64_t j)
+{
+    if (p->hadamard_n == 0)
+        return 0u;
+    if (p->sign_mode != ORC_SIGNS_PER_BLOCK)
+        return mask_signs(p->hadamard_n, p->sign_mask);
+    uint32_t key[2] = { (uint32_t)p->sign_seed, (uint32_t)(p->sign_seed >> 32) };
+    uint32_t ctr[4] = { (uint32_t)j, (uint32_t)(j >> 32), 0xFFFFFFFFu, 0xFFFFFFFEu };
+    uint32_t out[4];
+    orc_philox4x32_10(ctr, key, out);
+    return out[0];
 }
 
 /* ------------------------------------------------------------------------ */
@@ -225,10 +253,10 @@ uint32_t orc_sr_random(uint64_t seed, uint32_t stream, uint64_t b, int j, int bi
 /* One block: rotate, scale, divide by 2^e, round, sign-magnitude nibble.    */
 /* ------------------------------------------------------------------------ */
 void orc_quantize_block(const float x[32], const orc_qparams *p, uint64_t block_index,
-                        uint8_t nib[32], uint8_t *scale)
+                        uint64_t j, uint8_t nib[32], uint8_t *scale)
 {
     float y[32];
-    orc_rotate_block(x, p->hadamard_n, p->sign_mask, y);
+    orc_rotate_block_signs(x, p->hadamard_n, orc_block_signs(p, j), y);
     int sc = orc_scale_code(p->grid, y);
     *scale = (uint8_t)sc;
     if (sc == 0xFF) {
@@ -355,7 +383,7 @@ int orc_quantize_lines(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld
             int64_t local = line * nblk + jb;
             uint64_t b = (uint64_t)((line0 + line) * nblk + jb);
             gather_block(x, ld, axis, line, jb, xb);
-            orc_quantize_block(xb, p, b, nib, &scales[local]);
+            orc_quantize_block(xb, p, b, (uint64_t)jb, nib, &scales[local]);
             store_codes(codes + local * bbytes, fmt, p->grid, nib);
         }
     }
@@ -408,7 +436,7 @@ void orc_gemm_abt_f64(const double *a, const double *b, int64_t m, int64_t n, in
 }
 
 int orc_rotate(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
-               int hadamard_n, uint32_t sign_mask, float *y)
+               const orc_qparams *p, float *y)
 {
     if (check_shape(rows, cols, ld, axis))
         return -1;
@@ -418,7 +446,8 @@ int orc_rotate(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int ax
         for (int64_t jb = 0; jb < k / 32; ++jb) {
             float xb[32];
             gather_block(x, ld, axis, line, jb, xb);
-            orc_rotate_block(xb, hadamard_n, sign_mask, y + line * k + jb * 32);
+            orc_rotate_block_signs(xb, p->hadamard_n, orc_block_signs(p, (uint64_t)jb),
+                                   y + line * k + jb * 32);
         }
     }
     return 0;
@@ -447,7 +476,7 @@ int orc_stats(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axi
             float xb[32], y[32];
             uint8_t nib[32];
             gather_block(x, ld, axis, line, jb, xb);
-            orc_rotate_block(xb, p->hadamard_n, p->sign_mask, y);
+            orc_rotate_block_signs(xb, p->hadamard_n, orc_block_signs(p, (uint64_t)jb), y);
             int sc = scales[b];
             if (sc == 0xFF) {
                 out->n_nonfinite_blocks++;

@@ -40,6 +40,10 @@ enum { ORC_GRID_E2M1 = 0, ORC_GRID_E1M2 = 1, ORC_GRID_E2M1_MAX4 = 2, ORC_GRID_E2
 enum { ORC_RTNE = 0, ORC_SR = 1 };
 enum { ORC_FMT_FP4 = 0, ORC_FMT_E2M3 = 1 };
 enum { ORC_AXIS_ROW = 0, ORC_AXIS_COL = 1 };
+/* Random signs of the rotation: one n-bit mask shared by every block, or 32
+ * signs per block drawn from Philox by the block's index along the
+ * quantization axis (a sign vector as long as that axis). */
+enum { ORC_SIGNS_MASK = 0, ORC_SIGNS_PER_BLOCK = 1 };
 
 typedef struct {
     int32_t grid;        /* ORC_GRID_* */
@@ -49,6 +53,9 @@ typedef struct {
     uint64_t sr_seed;    /* Philox key */
     uint32_t sr_stream;  /* Philox counter word 3 */
     uint32_t sr_bits;    /* random bits per element: 8 or 16 */
+    uint32_t sign_mode;  /* ORC_SIGNS_MASK or ORC_SIGNS_PER_BLOCK */
+    uint32_t pad_;
+    uint64_t sign_seed;  /* Philox key of the per-block signs */
 } orc_qparams;
 
 typedef struct {
@@ -83,6 +90,13 @@ void orc_fwht_f32(float *u, int n);
 /* Rotation of one 32-block: per n-sub-block, sign flip, FWHT, times fl32(1/sqrt n).
  * n = 0 copies. */
 void orc_rotate_block(const float x[32], int n, uint32_t sign_mask, float y[32]);
+/* The same with one sign bit per position of the 32-block (bit i: position i). */
+void orc_rotate_block_signs(const float x[32], int n, uint32_t signs, float y[32]);
+/* The 32 sign bits of block j (its index along the quantization axis) under p:
+ * the mask repeated per n-sub-block, or word 0 of Philox4x32-10 with key
+ * (lo32(sign_seed), hi32(sign_seed)) and counter (lo32(j), hi32(j),
+ * 0xFFFFFFFF, 0xFFFFFFFE). */
+uint32_t orc_block_signs(const orc_qparams *p, uint64_t j);
 
 /* Shared E8M0 scale code of a rotated block (0xFF if any element is NaN/Inf). */
 int orc_scale_code(int grid, const float y[32]);
@@ -92,9 +106,11 @@ int orc_round_sr(int grid, double a, uint32_t r, int bits);
 /* The random value used for element j of block b under the SR stream. */
 uint32_t orc_sr_random(uint64_t seed, uint32_t stream, uint64_t b, int j, int bits);
 
-/* Quantize one 32-block.  nib[i] = sign<<3 | m. */
+/* Quantize one 32-block.  nib[i] = sign<<3 | m.  block_index keys the SR
+ * stream (the block's position in its scale array); j is the block's index
+ * along the quantization axis (it keys per-block signs). */
 void orc_quantize_block(const float x[32], const orc_qparams *p, uint64_t block_index,
-                        uint8_t nib[32], uint8_t *scale);
+                        uint64_t j, uint8_t nib[32], uint8_t *scale);
 
 /* E2M3 6-bit code (sign in bit 5) holding the value (-1)^s * G_m exactly. */
 int orc_e2m3_code(int grid, int nibble);
@@ -135,7 +151,7 @@ int orc_stats(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axi
 
 /* The fp32 rotated values y in output (line-major) order: [lines x k]. */
 int orc_rotate(const uint16_t *x, int64_t rows, int64_t cols, int64_t ld, int axis,
-               int hadamard_n, uint32_t sign_mask, float *y);
+               const orc_qparams *p, float *y);
 
 #ifdef __cplusplus
 }

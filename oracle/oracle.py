@@ -19,6 +19,7 @@ GRID_E2M1, GRID_E1M2, GRID_E2M1_MAX4, GRID_E2M1_MAX3 = 0, 1, 2, 3
 RTNE, SR = 0, 1
 FMT_FP4, FMT_E2M3 = 0, 1
 AXIS_ROW, AXIS_COL = 0, 1
+SIGNS_MASK, SIGNS_PER_BLOCK = 0, 1
 
 
 class QParams(C.Structure):
@@ -30,6 +31,9 @@ class QParams(C.Structure):
         ("sr_seed", C.c_uint64),
         ("sr_stream", C.c_uint32),
         ("sr_bits", C.c_uint32),
+        ("sign_mode", C.c_uint32),
+        ("pad_", C.c_uint32),
+        ("sign_seed", C.c_uint64),
     ]
 
 
@@ -74,12 +78,15 @@ def lib():
         L.orc_grid_top.argtypes = [C.c_int]
         L.orc_fwht_f32.argtypes = [P, C.c_int]
         L.orc_rotate_block.argtypes = [P, C.c_int, C.c_uint32, P]
+        L.orc_rotate_block_signs.argtypes = [P, C.c_int, C.c_uint32, P]
+        L.orc_block_signs.argtypes = [C.POINTER(QParams), C.c_uint64]
+        L.orc_block_signs.restype = C.c_uint32
         L.orc_scale_code.argtypes = [C.c_int, P]
         L.orc_round_rtne.argtypes = [C.c_int, C.c_double]
         L.orc_round_sr.argtypes = [C.c_int, C.c_double, C.c_uint32, C.c_int]
         L.orc_sr_random.argtypes = [C.c_uint64, C.c_uint32, C.c_uint64, C.c_int, C.c_int]
         L.orc_sr_random.restype = C.c_uint32
-        L.orc_quantize_block.argtypes = [P, C.POINTER(QParams), C.c_uint64, P, P]
+        L.orc_quantize_block.argtypes = [P, C.POINTER(QParams), C.c_uint64, C.c_uint64, P, P]
         L.orc_e2m3_code.argtypes = [C.c_int, C.c_int]
         L.orc_quantize.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int, P, P]
         L.orc_quantize_lines.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int,
@@ -89,7 +96,7 @@ def lib():
         L.orc_gemm_abt_f64.argtypes = [P, P, i64, i64, i64, P]
         L.orc_stats.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), C.c_int, P, P,
                                 C.POINTER(Stats)]
-        L.orc_rotate.argtypes = [P, i64, i64, i64, C.c_int, C.c_int, C.c_uint32, P]
+        L.orc_rotate.argtypes = [P, i64, i64, i64, C.c_int, C.POINTER(QParams), P]
         _lib = L
     return _lib
 
@@ -100,8 +107,9 @@ def _ptr(a: np.ndarray):
 
 
 def qparams(grid=GRID_E2M1, round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
-            sr_bits=16) -> QParams:
-    return QParams(grid, round, hadamard_n, sign_mask & 0xFFFFFFFF, sr_seed, sr_stream, sr_bits)
+            sr_bits=16, sign_mode=0, sign_seed=0) -> QParams:
+    return QParams(grid, round, hadamard_n, sign_mask & 0xFFFFFFFF, sr_seed, sr_stream, sr_bits,
+                   sign_mode, 0, sign_seed)
 
 
 # ---- scalar pieces --------------------------------------------------------
@@ -159,11 +167,25 @@ def sr_random(seed: int, stream: int, b: int, j: int, bits: int) -> int:
     return lib().orc_sr_random(seed, stream, b, j, bits)
 
 
-def quantize_block(x: np.ndarray, p: QParams, block_index: int = 0):
+def rotate_block_signs(x: np.ndarray, n: int, signs: int) -> np.ndarray:
+    """Rotation of one 32-block with one sign bit per position (bit i: position i)."""
+    xb = np.ascontiguousarray(x, dtype=np.float32)
+    assert xb.size == 32
+    y = np.zeros(32, dtype=np.float32)
+    lib().orc_rotate_block_signs(_ptr(xb), n, signs & 0xFFFFFFFF, _ptr(y))
+    return y
+
+
+def block_signs(p: QParams, j: int) -> int:
+    """The 32 sign bits of block j along the quantization axis under p."""
+    return lib().orc_block_signs(C.byref(p), j)
+
+
+def quantize_block(x: np.ndarray, p: QParams, block_index: int = 0, j: int = 0):
     xb = np.ascontiguousarray(x, dtype=np.float32)
     nib = np.zeros(32, dtype=np.uint8)
     sc = np.zeros(1, dtype=np.uint8)
-    lib().orc_quantize_block(_ptr(xb), C.byref(p), block_index, _ptr(nib), _ptr(sc))
+    lib().orc_quantize_block(_ptr(xb), C.byref(p), block_index, j, _ptr(nib), _ptr(sc))
     return nib, int(sc[0])
 
 
@@ -264,13 +286,15 @@ def gemm_abt_f64(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return c
 
 
-def rotate(x, axis: int, hadamard_n: int, sign_mask: int = 0) -> np.ndarray:
+def rotate(x, axis: int, hadamard_n: int, sign_mask: int = 0, sign_mode: int = 0,
+           sign_seed: int = 0) -> np.ndarray:
     xb = np.ascontiguousarray(_bf16_bits(x))
     rows, cols = xb.shape
     lines, k = (rows, cols) if axis == AXIS_ROW else (cols, rows)
     y = np.zeros((lines, k), dtype=np.float32)
-    rc = lib().orc_rotate(_ptr(xb), rows, cols, cols, axis, hadamard_n, sign_mask & 0xFFFFFFFF,
-                          _ptr(y))
+    p = qparams(hadamard_n=hadamard_n, sign_mask=sign_mask, sign_mode=sign_mode,
+                sign_seed=sign_seed)
+    rc = lib().orc_rotate(_ptr(xb), rows, cols, cols, axis, C.byref(p), _ptr(y))
     if rc != 0:
         raise ValueError("oracle rotate rejected shape")
     return y

@@ -169,3 +169,60 @@ def test_quantize_lines_matches_whole_tensor(orc):
         c, s = orc.quantize(x, axis, p)
         c2, s2 = orc.quantize_lines(x, axis, p, 17, 9)
         assert np.array_equal(c[17:26], c2) and np.array_equal(s[17:26], s2)
+
+
+@pytest.mark.parametrize("n", [16, 32])
+def test_rotate_block_signs_matches_dense_product(orc, n):
+    # y = c_n H_n D x per n-sub-block, D = diag(-1 where bit (position in the
+    # 32-block) of the sign word is set), against scipy's H in fp64
+    H = scipy.linalg.hadamard(n).astype(np.float64) / np.sqrt(n)
+    g = np.random.Generator(np.random.PCG64(90 + n))
+    for _ in range(100):
+        x = g.standard_normal(32).astype(np.float32)
+        s = int(g.integers(0, 1 << 32))
+        d = np.where((s >> np.arange(32)) & 1, -1.0, 1.0)
+        want = np.concatenate([H @ (d[b:b + n] * x[b:b + n].astype(np.float64))
+                               for b in range(0, 32, n)])
+        got = orc.rotate_block_signs(x, n, s).astype(np.float64)
+        assert np.max(np.abs(got - want)) <= 1e-6 * np.max(np.abs(want)) + 1e-12
+    # one mask for every block is the sign word that repeats it per sub-block
+    x = g.standard_normal(32).astype(np.float32)
+    m = 0xBEEF if n == 16 else 0xDEADBEEF
+    rep = (m | (m << 16)) if n == 16 else m
+    assert np.array_equal(orc.rotate_block(x, n, m), orc.rotate_block_signs(x, n, rep))
+
+
+def test_per_block_signs_vary_by_block_and_seed(orc):
+    p = orc.qparams(hadamard_n=32, sign_mode=orc.SIGNS_PER_BLOCK, sign_seed=12345)
+    words = [orc.block_signs(p, j) for j in range(4096)]
+    assert len(set(words)) == 4096                       # a new draw per block
+    bits = np.array([bin(w).count("1") for w in words])
+    assert abs(bits.mean() - 16) < 0.5                   # fair signs (sd of the mean ~0.045)
+    q = orc.qparams(hadamard_n=32, sign_mode=orc.SIGNS_PER_BLOCK, sign_seed=12346)
+    assert sum(orc.block_signs(q, j) == w for j, w in enumerate(words)) == 0
+    # mask mode ignores j and repeats the mask per sub-block
+    m = orc.qparams(hadamard_n=16, sign_mask=0x1234)
+    assert {orc.block_signs(m, j) for j in range(10)} == {0x12341234}
+
+
+@pytest.mark.parametrize("n", [16, 32])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_rotation_cancels_in_the_product(orc, n, mode):
+    # A [m x K] rotated along K row-wise and B [K x p] rotated along K
+    # column-wise with the same signs: the product is unchanged (the rotation
+    # is orthogonal), which pins that both orientations give position k the
+    # same sign, also when every block draws its own
+    from fp4_microscaling_quantization_amd import synth
+    m, K, p = 24, 256, 40
+    A = synth.f32_to_bf16_bits(np.random.Generator(np.random.PCG64(5)).standard_normal((m, K)).astype(np.float32))
+    B = synth.f32_to_bf16_bits(np.random.Generator(np.random.PCG64(6)).standard_normal((K, p)).astype(np.float32))
+    kw = dict(sign_mask=0xA5C3F00F, sign_mode=mode, sign_seed=777)
+    ra = orc.rotate(A, orc.AXIS_ROW, n, **kw).astype(np.float64)      # [m x K]
+    rb = orc.rotate(B, orc.AXIS_COL, n, **kw).astype(np.float64)      # [p x K]
+    want = synth.bf16_bits_to_f32(A).astype(np.float64) @ synth.bf16_bits_to_f32(B).astype(np.float64)
+    got = ra @ rb.T
+    assert np.linalg.norm(got - want) <= 1e-6 * np.linalg.norm(want)
+    if mode == 1:
+        # and the rotated operands differ from the single-mask ones
+        r0 = orc.rotate(A, orc.AXIS_ROW, n, sign_mask=0xA5C3F00F)
+        assert not np.array_equal(r0, ra.astype(np.float32))
