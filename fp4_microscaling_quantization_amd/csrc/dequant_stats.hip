@@ -151,7 +151,6 @@ __global__ __launch_bounds__(256) void k_stats(const uint16_t *__restrict__ x, i
     const int64_t k = axis == MXQ_AXIS_ROW ? cols : rows;
     const int64_t nbk = k / 32;
     const uint64_t nblocks = (uint64_t)(lines * nbk);
-    const uint32_t sg = HN ? (kn.sign_mask >> ((8 * pos) % (HN ? HN : 32))) & 0xFFu : 0u;
     const float top = grid == MXQ_GRID_E2M1 ? 6.0f
                       : grid == MXQ_GRID_E1M2 ? 3.5f
                       : grid == MXQ_GRID_E2M1_MAX4 ? 4.0f : 3.0f;
@@ -171,6 +170,7 @@ __global__ __launch_bounds__(256) void k_stats(const uint16_t *__restrict__ x, i
         float v[8];
         const int64_t line = valid ? (int64_t)(b / (uint64_t)nbk) : 0;
         const int64_t jb = valid ? (int64_t)b - line * nbk : 0;
+        const uint32_t sg = (block_signs<HN>(kn, (uint64_t)jb) >> (8 * pos)) & 0xFFu;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             uint32_t h = 0;

@@ -34,6 +34,9 @@ struct QKnobs {
     uint32_t sr_bits;  // 8 or 16
     int32_t emax;      // E2M1 family: 2, or 1 with a cap (E1M2 kernels use 1)
     float top2;        // E2M1 family: twice the top level (12, or 8 / 6 with a cap)
+    uint32_t sign_mode;          // MXQ_SIGNS_MASK: sign_mask holds the mask repeated per
+                                 // n-sub-block; MXQ_SIGNS_PER_BLOCK: drawn per block
+    uint32_t skey_lo, skey_hi;   // key of the per-block signs
 };
 
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
@@ -88,6 +91,20 @@ __device__ __forceinline__ Rand4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     Rand4 r;
     r.w[0] = c0; r.w[1] = c1; r.w[2] = c2; r.w[3] = c3;
     return r;
+}
+
+// The 32 sign bits of the block with index j along the quantization axis
+// (bit i: position i of the 32-block): the mask, repeated per n-sub-block on
+// the host, or word 0 of Philox4x32-10 at counter (lo32 j, hi32 j, ~0, ~1).
+template <int HN>
+__device__ __forceinline__ uint32_t block_signs(const QKnobs &kn, uint64_t j)
+{
+    if constexpr (HN == 0)
+        return 0u;
+    if (kn.sign_mode == 0)
+        return kn.sign_mask;
+    return philox4x32_10((uint32_t)j, (uint32_t)(j >> 32), 0xFFFFFFFFu, 0xFFFFFFFEu, kn.skey_lo,
+                         kn.skey_hi).w[0];
 }
 
 // ---- rounding of a normalized magnitude a = |y| 2^-e (0 <= a < 2^(emax+1)) --

@@ -50,6 +50,8 @@ mxq_status check_qconfig(const mxq_qconfig *cfg)
         return MXQ_ERR_UNSUPPORTED;
     if (cfg->round == MXQ_ROUND_SR && cfg->sr_bits != 8 && cfg->sr_bits != 16)
         return MXQ_ERR_UNSUPPORTED;
+    if (cfg->sign_mode != MXQ_SIGNS_MASK && cfg->sign_mode != MXQ_SIGNS_PER_BLOCK)
+        return MXQ_ERR_UNSUPPORTED;
     return MXQ_OK;
 }
 
@@ -75,7 +77,12 @@ mxq_status check_qtensor_out(const mxq_qtensor *t, int32_t grid, int64_t k)
 QKnobs make_knobs(const mxq_qconfig *cfg)
 {
     QKnobs kn;
-    kn.sign_mask = cfg->hadamard_n == 16 ? (cfg->sign_mask & 0xFFFFu) : cfg->sign_mask;
+    // one sign bit per position of the 32-block: a 16-bit mask repeats
+    kn.sign_mask = cfg->hadamard_n == 16 ? (cfg->sign_mask & 0xFFFFu) * 0x10001u
+                   : cfg->hadamard_n == 32 ? cfg->sign_mask : 0u;
+    kn.sign_mode = cfg->sign_mode;
+    kn.skey_lo = (uint32_t)cfg->sign_seed;
+    kn.skey_hi = (uint32_t)(cfg->sign_seed >> 32);
     kn.seed_lo = (uint32_t)cfg->sr_seed;
     kn.seed_hi = (uint32_t)(cfg->sr_seed >> 32);
     kn.stream = cfg->sr_stream;

@@ -313,9 +313,9 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
             hi[i] = hh[2] | (hh[3] << 16);
         }
     }
-    // random sign flips: position p = 16 pos + i takes bit p % HN of the mask
+    // random sign flips: position p = 16 pos + i takes bit p of the block's sign word
     if constexpr (HN > 0) {
-        const uint32_t sg = HN == 16 ? kn.sign_mask : kn.sign_mask >> (16 * pos);
+        const uint32_t sg = block_signs<HN>(kn, jb) >> (16 * pos);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const uint32_t f = ((sg >> i) & 1u) ? 0x80008000u : 0u;
@@ -408,7 +408,6 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int pos = lane & 1, pr = lane >> 1;
     const uint64_t base = ((uint64_t)blockIdx.x * 4 + wv) * (32 * U);
-    const uint32_t sg = HN == 16 ? kn.sign_mask : HN == 32 ? kn.sign_mask >> (16 * pos) : 0u;
     const float h = kn.sr_bits == 16 ? 0x1p-17f : 0x1p-9f;  // 2^-(B+1)
     const float h2 = 2.0f * h;
     constexpr bool kExact = FMT == MXQ_FMT_E2M3;
@@ -435,6 +434,7 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
                     w[k] = (uint32_t)x[off + 2 * k] | ((uint32_t)x[off + 2 * k + 1] << 16);
             }
         }
+        const uint32_t sg = block_signs<HN>(kn, jbk[u]) >> (16 * pos);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             v[u][2 * k] = as_f((w[k] << 16) ^ (((sg >> (2 * k)) & 1u) << 31));
@@ -546,7 +546,7 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
                 make_uint2(lo[i], hi[i]);
         }
         if constexpr (HN > 0) {
-            const uint32_t sg = HN == 16 ? kn.sign_mask : kn.sign_mask >> (16 * pos);
+            const uint32_t sg = block_signs<HN>(kn, jb) >> (16 * pos);
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const uint32_t f = ((sg >> i) & 1u) ? 0x80008000u : 0u;
@@ -616,7 +616,6 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
     // p = t >> 1 takes block p % 4 of rows p / 4 + 32 u, u = 0..3
     const uint64_t nbr = (uint64_t)cols >> 5;
     const int p = t >> 1;
-    const uint32_t sgr = HN == 16 ? kn.sign_mask : HN == 32 ? kn.sign_mask >> (16 * pos) : 0u;
     constexpr bool kExactR = FMTR == MXQ_FMT_E2M3;
     float v[4][16];
     bool ok[4];
@@ -627,6 +626,7 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
         rline[u] = (uint64_t)(row0 + lr);
         rjb[u] = (uint64_t)(col0 / 32 + lb);
         ok[u] = (int64_t)rline[u] < rows && rjb[u] < nbr;
+        const uint32_t sgr = block_signs<HN>(kn, rjb[u]) >> (16 * pos);
         const uint8_t *src = tile + lr * kTileRS;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {

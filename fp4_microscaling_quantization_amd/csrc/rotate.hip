@@ -26,7 +26,7 @@ __device__ __forceinline__ uint32_t bf16_rne(float f)
 
 template <int HN, int OUT>
 __global__ __launch_bounds__(256) void k_rotate_row(const uint16_t *__restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t ld, int vec, uint32_t mask,
+                                                    int64_t cols, int64_t ld, int vec, QKnobs kn,
                                                     uint8_t *__restrict__ out, int64_t ldo, int vst)
 {
     const int t = threadIdx.x, pos = t & 3;
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void k_rotate_row(const uint16_t *__restrict__
                 w[k] = (uint32_t)x[off + 2 * k] | ((uint32_t)x[off + 2 * k + 1] << 16);
         }
     }
-    const uint32_t sg = (mask >> ((8 * pos) % HN)) & 0xFFu;
+    const uint32_t sg = (block_signs<HN>(kn, (uint64_t)jb) >> (8 * pos)) & 0xFFu;
     float v[8];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_rotate_row(const uint16_t *__restrict__
 
 template <int HN, int OUT>
 __global__ __launch_bounds__(256) void k_rotate_col(const uint16_t *__restrict__ x, int64_t rows,
-                                                    int64_t cols, int64_t ld, int vec, uint32_t mask,
+                                                    int64_t cols, int64_t ld, int vec, QKnobs kn,
                                                     uint8_t *__restrict__ out, int64_t ldo, int vst)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(256) void k_rotate_col(const uint16_t *__restrict__
             hi[i] = h[2] | (h[3] << 16);
         }
     }
-    const uint32_t sg = HN == 16 ? mask : mask >> (16 * pos);
+    const uint32_t sg = block_signs<HN>(kn, (uint64_t)(rband >> 5)) >> (16 * pos);
     const float c = HN == 16 ? 0.25f : as_f(0x3E3504F3u);
     float y[4][16];
 #pragma unroll
@@ -161,7 +161,7 @@ namespace {
 
 template <int HN, int OUT>
 void launch_rotate(int32_t axis, const uint16_t *x, int64_t rows, int64_t cols, int64_t ld,
-                   uint32_t mask, uint8_t *out, int64_t ldo, hipStream_t s)
+                   const QKnobs &kn, uint8_t *out, int64_t ldo, hipStream_t s)
 {
     // vector stores need every row's output to keep their alignment
     constexpr int esz = OUT == MXQ_OUT_F32 ? 4 : 2;
@@ -170,12 +170,12 @@ void launch_rotate(int32_t axis, const uint16_t *x, int64_t rows, int64_t cols, 
         const int vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0 && ld % 8 == 0) ? 1 : 0;
         const int64_t nblocks = rows * (cols / 32);
         hipLaunchKernelGGL((k_rotate_row<HN, OUT>), dim3((unsigned)((nblocks + 63) / 64)),
-                           dim3(256), 0, s, x, rows, cols, ld, vec, mask, out, ldo, vst);
+                           dim3(256), 0, s, x, rows, cols, ld, vec, kn, out, ldo, vst);
     } else {
         const int vec = (reinterpret_cast<uintptr_t>(x) % 8 == 0 && ld % 4 == 0) ? 1 : 0;
         const dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
         hipLaunchKernelGGL((k_rotate_col<HN, OUT>), grid, dim3(256), 0, s, x, rows, cols, ld, vec,
-                           mask, out, ldo, vst);
+                           kn, out, ldo, vst);
     }
 }
 
@@ -192,6 +192,8 @@ extern "C" mxq_status mxq_rotate(const mxq_qconfig *cfg, const void *x, int64_t 
     if (!cfg || !x || !out)
         return MXQ_ERR_NULL;
     if (cfg->hadamard_n != 16 && cfg->hadamard_n != 32)
+        return MXQ_ERR_UNSUPPORTED;
+    if (cfg->sign_mode != MXQ_SIGNS_MASK && cfg->sign_mode != MXQ_SIGNS_PER_BLOCK)
         return MXQ_ERR_UNSUPPORTED;
     if ((axis != MXQ_AXIS_ROW && axis != MXQ_AXIS_COL) ||
         (out_dtype != MXQ_OUT_F32 && out_dtype != MXQ_OUT_BF16))
@@ -210,17 +212,17 @@ extern "C" mxq_status mxq_rotate(const mxq_qconfig *cfg, const void *x, int64_t 
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     uint8_t *o = static_cast<uint8_t *>(out);
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const uint32_t mask = cfg->hadamard_n == 16 ? (cfg->sign_mask & 0xFFFFu) : cfg->sign_mask;
+    const QKnobs kn = make_knobs(cfg);
     if (cfg->hadamard_n == 16) {
         if (out_dtype == MXQ_OUT_F32)
-            launch_rotate<16, MXQ_OUT_F32>(axis, xx, rows, cols, ld_x, mask, o, ld_out, s);
+            launch_rotate<16, MXQ_OUT_F32>(axis, xx, rows, cols, ld_x, kn, o, ld_out, s);
         else
-            launch_rotate<16, MXQ_OUT_BF16>(axis, xx, rows, cols, ld_x, mask, o, ld_out, s);
+            launch_rotate<16, MXQ_OUT_BF16>(axis, xx, rows, cols, ld_x, kn, o, ld_out, s);
     } else {
         if (out_dtype == MXQ_OUT_F32)
-            launch_rotate<32, MXQ_OUT_F32>(axis, xx, rows, cols, ld_x, mask, o, ld_out, s);
+            launch_rotate<32, MXQ_OUT_F32>(axis, xx, rows, cols, ld_x, kn, o, ld_out, s);
         else
-            launch_rotate<32, MXQ_OUT_BF16>(axis, xx, rows, cols, ld_x, mask, o, ld_out, s);
+            launch_rotate<32, MXQ_OUT_BF16>(axis, xx, rows, cols, ld_x, kn, o, ld_out, s);
     }
     return hipGetLastError() == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
 }

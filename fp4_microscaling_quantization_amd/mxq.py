@@ -20,6 +20,7 @@ FMT_FP4, FMT_E2M3 = 0, 1
 LAYOUT_ROWS, LAYOUT_MFMA = 0, 1
 AXIS_ROW, AXIS_COL = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
+SIGNS_MASK, SIGNS_PER_BLOCK = 0, 1
 
 SYMBOLS = ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "mxq_bias_stats",
            "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_rht_sign_mask", "mxq_rotate",
@@ -29,7 +30,8 @@ SYMBOLS = ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "
 class QConfig(C.Structure):
     _fields_ = [("grid", C.c_int32), ("round", C.c_int32), ("hadamard_n", C.c_int32),
                 ("sign_mask", C.c_uint32), ("sr_seed", C.c_uint64), ("sr_stream", C.c_uint32),
-                ("sr_bits", C.c_uint32)]
+                ("sr_bits", C.c_uint32), ("sign_mode", C.c_uint32), ("reserved", C.c_uint32),
+                ("sign_seed", C.c_uint64)]
 
 
 class QTensor(C.Structure):
@@ -106,8 +108,9 @@ def _stream(stream=None):
 
 
 def qconfig(grid=GRID_E2M1, round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
-            sr_bits=16) -> QConfig:
-    return QConfig(grid, round, hadamard_n, sign_mask & 0xFFFFFFFF, sr_seed, sr_stream, sr_bits)
+            sr_bits=16, sign_mode=SIGNS_MASK, sign_seed=0) -> QConfig:
+    return QConfig(grid, round, hadamard_n, sign_mask & 0xFFFFFFFF, sr_seed, sr_stream, sr_bits,
+                   sign_mode, 0, sign_seed)
 
 
 def block_bytes(fmt: int) -> int:
@@ -195,9 +198,11 @@ def prepare_quantize(cfg: QConfig, x, row=None, col=None, stream=None):
 
 def quantize(x, grid=GRID_E2M1, round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
              sr_bits=16, row=True, col=False, row_fmt=FMT_FP4, col_fmt=FMT_FP4,
-             row_layout=LAYOUT_ROWS, col_layout=LAYOUT_ROWS, fill=None, stream=None):
+             row_layout=LAYOUT_ROWS, col_layout=LAYOUT_ROWS, fill=None, stream=None,
+             sign_mode=SIGNS_MASK, sign_seed=0):
     """Quantize a 2-D bf16 CUDA tensor; returns {'row': (codes, scales), 'col': (...)}."""
-    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits)
+    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits, sign_mode,
+                  sign_seed)
     rows, cols = x.shape
     out = {}
     r = c = None
@@ -278,12 +283,13 @@ def gemm_abt(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid,
 
 
 def rotate(x, axis: int, hadamard_n: int, sign_mask: int = 0, out_dtype=OUT_F32, out=None,
-           stream=None):
+           stream=None, sign_mode=SIGNS_MASK, sign_seed=0):
     """The block rotation alone, in x's orientation (fp32 or bf16 out)."""
     import torch
     dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
     o = torch.empty(x.shape, dtype=dt, device=x.device) if out is None else out
-    cfg = qconfig(hadamard_n=hadamard_n, sign_mask=sign_mask)
+    cfg = qconfig(hadamard_n=hadamard_n, sign_mask=sign_mask, sign_mode=sign_mode,
+                  sign_seed=sign_seed)
     _check("mxq_rotate", lib().mxq_rotate(C.byref(cfg), _ptr(x), x.shape[0], x.shape[1],
                                           x.stride(0), axis, out_dtype, _ptr(o), o.stride(0),
                                           _stream(stream)))
@@ -309,9 +315,11 @@ def rht_sign_mask(seed: int, n: int) -> int:
 
 
 def bias_stats(x, axis: int, codes, scales, fmt: int, grid=GRID_E2M1, round=RTNE, hadamard_n=0,
-               sign_mask=0, sr_seed=0, sr_stream=0, sr_bits=16, stream=None) -> dict:
+               sign_mask=0, sr_seed=0, sr_stream=0, sr_bits=16, stream=None,
+               sign_mode=SIGNS_MASK, sign_seed=0) -> dict:
     import torch
-    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits)
+    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits, sign_mode,
+                  sign_seed)
     rows, cols = x.shape
     wsb = lib().mxq_bias_stats_workspace_size(rows, cols, axis)
     ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device=x.device)

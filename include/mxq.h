@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 1
+#define MXQ_ABI_VERSION 2
 
 typedef int32_t mxq_status;
 #define MXQ_OK 0
@@ -109,14 +109,27 @@ typedef int32_t mxq_status;
 #define MXQ_OUT_F32 0
 #define MXQ_OUT_BF16 1
 
+#define MXQ_SIGNS_MASK 0        /* one sign mask shared by every block        */
+#define MXQ_SIGNS_PER_BLOCK 1   /* each block draws its own 32 signs          */
+
 /* Quantizer knobs.
  * hadamard_n: 0 (no rotation), 16 or 32.  Each n-element sub-block of a
  *   32-block is replaced by fl32(1/sqrt(n)) * H_n * (D x), H_n the Sylvester
  *   Hadamard matrix in natural order, computed in fp32 by butterfly stages of
  *   stride 1, 2, 4, ... (the stage order fixes the fp32 rounding).
- * sign_mask: D = diag(d_i), d_i = -1 where bit (i mod n) is set; 0 gives the
- *   deterministic Hadamard rotation, a random mask the randomized one (RHT).
- *   The same mask must be used for both operands of one GEMM.
+ * sign_mode, sign_mask, sign_seed: D = diag(d_i) for position i of the
+ *   32-block, the random sign inversion before the transform (htx.com news,
+ *   "Experimento de diagnostico").
+ *   MXQ_SIGNS_MASK: d_i = -1 where bit (i mod n) of sign_mask is set, the
+ *     same for every block; mask 0 gives the deterministic Hadamard
+ *     rotation, a random mask the randomized one (RHT).
+ *   MXQ_SIGNS_PER_BLOCK: a sign vector as long as the quantization axis.
+ *     The block with index j along that axis (the same j on every line)
+ *     takes d_i = -1 where bit i of word 0 of Philox4x32-10 is set, with key
+ *     (lo32(sign_seed), hi32(sign_seed)) and counter (lo32(j), hi32(j),
+ *     0xFFFFFFFF, 0xFFFFFFFE).
+ *   Both operands of one GEMM must use the same signs along their shared
+ *   axis (same mode and mask or seed); the rotation then cancels.
  * sr_seed, sr_stream, sr_bits: the stochastic-rounding stream.  Element j of
  *   the block with index b (its position in the scale array, row-major) takes
  *   Philox4x32-10 with key (lo32(seed), hi32(seed)):
@@ -132,6 +145,9 @@ typedef struct {
     uint64_t sr_seed;
     uint32_t sr_stream;
     uint32_t sr_bits;
+    uint32_t sign_mode;   /* MXQ_SIGNS_* */
+    uint32_t reserved;    /* 0 */
+    uint64_t sign_seed;   /* key of the per-block signs */
 } mxq_qconfig;
 
 /* A block-quantized tensor of `lines` lines, each `k` elements long (k % 32

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(mxq_lib):
 
 def test_abi_version_and_status_strings(mxq_lib):
     L = mxq_lib.lib()
-    assert L.mxq_abi_version() == 1
+    assert L.mxq_abi_version() == 2
     for s in range(7):
         assert mxq_lib.status_string(s)
     assert mxq_lib.status_string(0) == "ok"
@@ -58,6 +58,7 @@ def test_quantize_validation(mxq_lib):
     assert q(good, x=None) == M.ERR_NULL
     assert q(good, row=None, col=None) == M.ERR_NULL
     assert q(M.qconfig(grid=4)) == M.ERR_UNSUPPORTED
+    assert q(M.qconfig(sign_mode=2)) == M.ERR_UNSUPPORTED
     assert q(M.qconfig(round=5)) == M.ERR_UNSUPPORTED
     assert q(M.qconfig(hadamard_n=8)) == M.ERR_UNSUPPORTED
     assert q(M.qconfig(round=M.SR, sr_bits=12)) == M.ERR_UNSUPPORTED

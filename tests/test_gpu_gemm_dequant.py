@@ -137,13 +137,15 @@ def test_dequantize_exact(orc, fmt, grid):
 
 
 @pytest.mark.parametrize("axis", [0, 1], ids=["row", "col"])
-@pytest.mark.parametrize("knobs", [(0, 0, 16), (1, 0, 16), (1, 1, 32), (0, 1, 0), (2, 0, 16),
-                                   (3, 1, 32), (3, 0, 0)])
+@pytest.mark.parametrize("knobs", [(0, 0, 16, 0), (1, 0, 16, 0), (1, 1, 32, 0), (0, 1, 0, 0),
+                                   (2, 0, 16, 0), (3, 1, 32, 0), (3, 0, 0, 0), (1, 1, 16, 1),
+                                   (0, 0, 32, 1)])
 def test_bias_stats_match_oracle(orc, axis, knobs):
     from fp4_microscaling_quantization_amd import mxq
-    grid, rnd, n = knobs
+    grid, rnd, n, smode = knobs
     x = synth.normal_outlier_channels(192, 256, seed=2, ch_seed=3, frac=0.02)
-    kw = dict(grid=grid, round=rnd, hadamard_n=n, sign_mask=synth.sign_mask(9, n), sr_seed=4)
+    kw = dict(grid=grid, round=rnd, hadamard_n=n, sign_mask=synth.sign_mask(9, n), sr_seed=4,
+              sign_mode=smode, sign_seed=0x77)
     say("stats", axis, knobs)
     xt = to_dev_bf16(x)
     key = "row" if axis == 0 else "col"

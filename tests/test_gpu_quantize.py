@@ -93,6 +93,21 @@ def test_capped_e2m1_parity(orc, shape, knobs):
                    tag="cap-dual")
 
 
+@pytest.mark.parametrize("shape", [(96, 160), (256, 4096), (33, 4128), (4096, 64)])
+@pytest.mark.parametrize("knobs", [(0, 0, 16), (1, 1, 32), (1, 0, 16), (2, 1, 16), (0, 0, 32)],
+                         ids=_knob_id)
+def test_per_block_signs_parity(orc, shape, knobs):
+    # every 32-block along the quantization axis draws its own 32 signs
+    rows, cols = shape
+    x = synth.normal_outlier_channels(rows, cols, seed=cols, ch_seed=rows, frac=0.01)
+    for fmt in (0, 1):
+        p = dict(_params(orc, *knobs, seed=3), sign_mode=1, sign_seed=0xABCDEF0123 + fmt)
+        _check(orc, x, p, row_fmt=fmt, tag="signs-row")
+        if rows % 32 == 0:
+            _check(orc, x, p, col_fmt=fmt, tag="signs-col")
+            _check(orc, x, p, row_fmt=fmt, col_fmt=1 - fmt, tag="signs-dual")
+
+
 @pytest.mark.parametrize("knobs", KNOBS + KNOBS_CAP, ids=_knob_id)
 def test_special_values(orc, knobs):
     x = special_matrix(96, 160, seed=11)

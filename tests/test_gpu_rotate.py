@@ -18,19 +18,20 @@ def _bf16_rne_bits(y: np.ndarray) -> np.ndarray:
     return np.where(nan, np.uint16(0x7FC0), r), nan
 
 
-def _check(orc, x, axis, n, mask, tag):
+def _check(orc, x, axis, n, mask, tag, sign_mode=0, sign_seed=0):
     from fp4_microscaling_quantization_amd import mxq
-    say("rotate", tag, x.shape, axis, n)
+    say("rotate", tag, x.shape, axis, n, sign_mode)
     xt = to_dev_bf16(x)
-    ref = orc.rotate(x, axis, n, mask)
+    sk = dict(sign_mode=sign_mode, sign_seed=sign_seed)
+    ref = orc.rotate(x, axis, n, mask, **sk)
     if axis == 1:
         ref = np.ascontiguousarray(ref.T)          # the oracle is line-major
-    got = host(mxq.rotate(xt, axis, n, mask, mxq.OUT_F32))
+    got = host(mxq.rotate(xt, axis, n, mask, mxq.OUT_F32, **sk))
     nan = np.isnan(ref)
     assert np.array_equal(np.isnan(got), nan)
     assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32)), tag
     import torch
-    gb = host(mxq.rotate(xt, axis, n, mask, mxq.OUT_BF16).view(torch.int16))
+    gb = host(mxq.rotate(xt, axis, n, mask, mxq.OUT_BF16, **sk).view(torch.int16))
     rb, rnan = _bf16_rne_bits(ref)
     gb = gb.view(np.uint16)
     gnan = ((gb & 0x7FFF) > 0x7F80)
@@ -52,3 +53,10 @@ def test_rotate_special_values(orc, n):
     x = special_matrix(96, 160, seed=13)
     _check(orc, x, 0, n, synth.sign_mask(5, n), "special-row")
     _check(orc, x, 1, n, synth.sign_mask(6, n), "special-col")
+
+
+@pytest.mark.parametrize("axis", [0, 1], ids=["row", "col"])
+@pytest.mark.parametrize("n", [16, 32])
+def test_rotate_per_block_signs(orc, axis, n):
+    x = synth.normal(256, 384, seed=61 + n)
+    _check(orc, x, axis, n, 0, "per-block", sign_mode=1, sign_seed=0x5151 + axis)
