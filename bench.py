@@ -50,14 +50,14 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     "e1m2": {
-        "quantize_dy_col_sr": {"read": 67362489, "write": 26214830, "sha": "aea97bc8ac5ef34f"},
-        "quantize_x_col_rtne": {"read": 67270936, "write": 26218752, "sha": "aea97bc8ac5ef34f"},
-        "wgrad_gemm": {"read": 157553937, "write": 67116562, "sha": "89476f4b16a9b7b1"},
+        "quantize_dy_col_sr": {"read": 67342862, "write": 26217801, "sha": "91f87440f40d3025"},
+        "quantize_x_col_rtne": {"read": 67277419, "write": 26215077, "sha": "91f87440f40d3025"},
+        "wgrad_gemm": {"read": 157554090, "write": 67113865, "sha": "89476f4b16a9b7b1"},
     },
     "e2m1": {
-        "quantize_dy_col_sr": {"read": 67387254, "write": 17826633, "sha": "aea97bc8ac5ef34f"},
-        "quantize_x_col_rtne": {"read": 67267743, "write": 17834779, "sha": "aea97bc8ac5ef34f"},
-        "wgrad_gemm": {"read": 107207982, "write": 67113216, "sha": "89476f4b16a9b7b1"},
+        "quantize_dy_col_sr": {"read": 67374143, "write": 17825810, "sha": "91f87440f40d3025"},
+        "quantize_x_col_rtne": {"read": 67268839, "write": 17826798, "sha": "91f87440f40d3025"},
+        "wgrad_gemm": {"read": 107207110, "write": 67117285, "sha": "89476f4b16a9b7b1"},
     },
 }
 
@@ -439,7 +439,10 @@ def quality_report(torch, mxq, synth, dev):
     ws = synth.sign_mask(synth.SIGNS_W, 32)
     rep["w_14336x4096_h32_signs"] = {
         g: {"row": summarize(stats(w, 0, grid=v, hadamard_n=32, sign_mask=ws), v),
-            "col": summarize(stats(w, 1, grid=v, hadamard_n=32, sign_mask=ws), v)}
+            "col": summarize(stats(w, 1, grid=v, hadamard_n=32, sign_mask=ws), v),
+            "row_per_block_signs": summarize(stats(w, 0, grid=v, hadamard_n=32,
+                                                   sign_mode=mxq.SIGNS_PER_BLOCK,
+                                                   sign_seed=synth.SIGNS_W), v)}
         for g, v in grids.items()}
     del w
     dy = to_dev(synth.dy_16384x4096())
