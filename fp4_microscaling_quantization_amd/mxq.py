@@ -61,7 +61,7 @@ def lib() -> C.CDLL:
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"libmxq.so is not built ({LIB_PATH}); run "
-                              "`python -c 'import __graft_entry__ as g; g.build()'` first")
+                              "`python -m fp4_microscaling_quantization_amd.build` first")
         L = C.CDLL(LIB_PATH)
         P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         L.mxq_quantize.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, C.POINTER(QTensor),
