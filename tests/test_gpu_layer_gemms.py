@@ -101,3 +101,38 @@ def test_gemm_abt_is_the_wgrad_product():
     b = mxq.wgrad_gemm(q[0], q[1], 1, 1, q[0], q[1], 1, 1, layout=mxq.LAYOUT_MFMA, m=384, n=384, k=512)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("sign_mode", [0, 1], ids=["mask", "per-block"])
+def test_rotation_cancels_in_the_gpu_product(orc, sign_mode):
+    # Fprop with both operands rotated along K by the same signs: the GPU
+    # product matches the oracle pipeline and approximates the unrotated fp64
+    # X W^T to within quantization noise; with W's signs drawn from another
+    # seed the rotation no longer cancels and the result is noise
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    m, n, k = 512, 768, 1024
+    x = synth.normal(m, k, seed=51)
+    w = synth.normal(n, k, seed=52, std=0.02)
+    kn = dict(grid=1, round=0, hadamard_n=32, sign_mask=synth.sign_mask(53, 32),
+              sign_mode=sign_mode, sign_seed=54)
+    say("cancel", sign_mode)
+
+    def fprop(kx, kw):
+        qx = mxq.quantize(to_dev_bf16(x), row=True, row_fmt=1, row_layout=mxq.LAYOUT_MFMA, **kx)["row"]
+        qw = mxq.quantize(to_dev_bf16(w), row=True, row_fmt=1, row_layout=mxq.LAYOUT_MFMA, **kw)["row"]
+        y = mxq.gemm_abt(qx[0], qx[1], 1, 1, qw[0], qw[1], 1, 1, layout=mxq.LAYOUT_MFMA, m=m, n=n, k=k)
+        torch.cuda.synchronize()
+        return y.cpu().numpy().astype(np.float64)
+
+    y = fprop(kn, kn)
+    p = orc.qparams(**kn)
+    A = orc.dequantize(*orc.quantize(x, orc.AXIS_ROW, p, 1), 1, 1)
+    B = orc.dequantize(*orc.quantize(w, orc.AXIS_ROW, p, 1), 1, 1)
+    ref = orc.gemm_abt_f64(A, B)
+    assert np.linalg.norm(y - ref) <= 1e-6 * np.linalg.norm(ref)
+    exact = synth.bf16_bits_to_f32(x).astype(np.float64) @ synth.bf16_bits_to_f32(w).astype(np.float64).T
+    sqnr = lambda v: 10 * np.log10(np.sum(exact ** 2) / np.sum((v - exact) ** 2))
+    assert sqnr(y) > 12.0, sqnr(y)
+    other = dict(kn, sign_mask=synth.sign_mask(55, 32), sign_seed=56)
+    assert sqnr(fprop(kn, other)) < 1.0
