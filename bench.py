@@ -14,11 +14,12 @@ last-level cache.
 
 Timing: W untimed warmup steps; then the timed region, K whole steps back to
 back between two HIP events (ms_per_step); then each kernel K times back to
-back between two events, which gives its average launch duration without
-event records between launches.
+back between two events (after a 50 ms idle gap), which gives its average
+launch duration without event records between launches.
 
 The JSON line reports the fused quantize bandwidth as `value` (algorithmic
-bytes of the two quantize launches / their average durations), the GEMM
+bytes of both operands / the average duration of the one batched launch that
+quantizes them), the GEMM
 rate under `gemm`, the roofline of the dominant kernel and of each kernel,
 and the CPU oracle timed on a bounded sample as `cpu_baseline`.
 """
@@ -45,18 +46,14 @@ T, N, K = 8192, 4096, 4096     # tokens, out features (dY cols), in features (X 
 # and a kernel whose sources have changed since reports traffic null.
 KERNEL_SOURCES = {
     "wgrad_gemm": ["csrc/wgrad_gemm.hip"],
-    "quantize_dy_col_sr": ["csrc/quantize_col.hip", "csrc/mxq_device.hpp", "csrc/quant_out.hpp"],
-    "quantize_x_col_rtne": ["csrc/quantize_col.hip", "csrc/mxq_device.hpp", "csrc/quant_out.hpp"],
+    "quantize_pair_col": ["csrc/quantize_col.hip", "csrc/mxq_device.hpp", "csrc/quant_out.hpp",
+                          "csrc/mxq_host.hpp"],
 }
 MEASURED_TRAFFIC = {
     "e1m2": {
-        "quantize_dy_col_sr": {"read": 67342862, "write": 26217801, "sha": "91f87440f40d3025"},
-        "quantize_x_col_rtne": {"read": 67277419, "write": 26215077, "sha": "91f87440f40d3025"},
         "wgrad_gemm": {"read": 157554090, "write": 67113865, "sha": "89476f4b16a9b7b1"},
     },
     "e2m1": {
-        "quantize_dy_col_sr": {"read": 67374143, "write": 17825810, "sha": "91f87440f40d3025"},
-        "quantize_x_col_rtne": {"read": 67268839, "write": 17826798, "sha": "91f87440f40d3025"},
         "wgrad_gemm": {"read": 107207110, "write": 67117285, "sha": "89476f4b16a9b7b1"},
     },
 }
@@ -201,22 +198,27 @@ def main():
         sets.append((dy, xx, qd, qx, c))
     torch.cuda.synchronize()
 
-    # the three launches of each set, marshalled once so that the host stays
-    # ahead of the GPU and the events time the kernels, not the launch path
+    # the launches of each set, marshalled once so that the host stays ahead
+    # of the GPU and the events time the kernels, not the launch path.  A step
+    # is one batched quantize launch of both operands (dY's SR tiles first,
+    # then X's RTNE tiles) and the GEMM; the two separate quantize launches
+    # are timed as well, for comparison.
     calls = []
     for dy, xx, qd, qx, c in sets:
+        col_dy = (qd[0], qd[1], fmt, mxq.LAYOUT_MFMA)
+        col_x = (qx[0], qx[1], fmt, mxq.LAYOUT_MFMA)
         calls.append((
-            mxq.prepare_quantize(cfg_dy, dy, col=(qd[0], qd[1], fmt, mxq.LAYOUT_MFMA)),
-            mxq.prepare_quantize(cfg_x, xx, col=(qx[0], qx[1], fmt, mxq.LAYOUT_MFMA)),
+            mxq.prepare_quantize_batch([(cfg_dy, dy, None, col_dy), (cfg_x, xx, None, col_x)]),
             mxq.prepare_wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, c,
-                                   mxq.LAYOUT_MFMA, N, K, T)))
+                                   mxq.LAYOUT_MFMA, N, K, T),
+            mxq.prepare_quantize(cfg_dy, dy, col=col_dy),
+            mxq.prepare_quantize(cfg_x, xx, col=col_x)))
 
     stream = torch.cuda.current_stream()
 
     def step(i):
-        q_dy, q_x, gemm = calls[i % len(calls)]
-        q_dy()
-        q_x()
+        q_pair, gemm = calls[i % len(calls)][:2]
+        q_pair()
         gemm()
 
     def timed(fn, n):
@@ -239,25 +241,25 @@ def main():
     t_steps = timed(step, args.steps)
     wall = time.perf_counter() - w0
     # each kernel's average launch duration: K launches of it back to back over
-    # the same rotating sets (no event between launches)
-    t_qdy = timed(lambda i: calls[i % len(calls)][0](), args.steps) / args.steps
-    t_qx = timed(lambda i: calls[i % len(calls)][1](), args.steps) / args.steps
-    t_gm = timed(lambda i: calls[i % len(calls)][2](), args.steps) / args.steps
+    # the same rotating sets (no event between launches); every loop starts
+    # after the same short idle gap, so none inherits the power state the
+    # loop before it left
+    def own_loop(j):
+        time.sleep(0.05)
+        return timed(lambda i: calls[i % len(calls)][j](), args.steps) / args.steps
+    t_qp, t_gm, t_qdy, t_qx = (own_loop(j) for j in range(4))
 
     elems = T * N
-    qbytes = elems * quant_bytes_per_elem(fmt)                           # per launch
+    qbytes = elems * quant_bytes_per_elem(fmt)                           # per operand
     flops = 2.0 * N * K * T
-    q_gbs = 2 * qbytes / (t_qdy + t_qx) / 1e9
+    q_gbs = 2 * qbytes / t_qp / 1e9
     g_tflops = flops / t_gm / 1e12
     mfma_peak = MFMA_PEAK_TFLOPS["fp6" if fmt == mxq.FMT_E2M3 else "fp4"]
 
     kernels = {
-        "quantize_dy_col_sr": {"bound": "hbm", "avg_us": t_qdy * 1e6,
-                               "achieved": qbytes / t_qdy / 1e9, "peak": HBM_PEAK_GBS,
-                               "unit": "GB/s"},
-        "quantize_x_col_rtne": {"bound": "hbm", "avg_us": t_qx * 1e6,
-                                "achieved": qbytes / t_qx / 1e9, "peak": HBM_PEAK_GBS,
-                                "unit": "GB/s"},
+        "quantize_pair_col": {"bound": "hbm", "avg_us": t_qp * 1e6,
+                              "achieved": 2 * qbytes / t_qp / 1e9, "peak": HBM_PEAK_GBS,
+                              "unit": "GB/s"},
         "wgrad_gemm": {"bound": "mfma", "avg_us": t_gm * 1e6,
                        "achieved": flops / t_gm / 1e12, "peak": mfma_peak, "unit": "TFLOP/s"},
     }
@@ -297,7 +299,11 @@ def main():
         },
         "step": {"gpu_ms": round(t_steps / args.steps * 1e3, 4),
                  "wall_ms": round(wall / args.steps * 1e3, 4),
-                 "kernels_ms": round((t_qdy + t_qx + t_gm) * 1e3, 4)},
+                 "kernels_ms": round((t_qp + t_gm) * 1e3, 4)},
+        "quantize_separate": {
+            "dy_col_sr_us": round(t_qdy * 1e6, 3), "x_col_rtne_us": round(t_qx * 1e6, 3),
+            "both_gbs": round(2 * qbytes / (t_qdy + t_qx) / 1e9, 2),
+            "batched_speedup": round((t_qdy + t_qx) / t_qp, 4)},
         "gemm": {"value": round(g_tflops, 2), "unit": "TFLOP/s", "peak": mfma_peak,
                  "frac": round(g_tflops / mfma_peak, 4)},
         "roofline": dom,

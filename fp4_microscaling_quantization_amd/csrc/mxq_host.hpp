@@ -25,6 +25,29 @@ struct ColLaunch {
 };
 hipError_t launch_quant_col(int grid, int round, int hn, const ColLaunch &q);
 
+// One job of a batched column-wise launch: a ColLaunch's tensor plus its
+// rounding and its range of 128 x 128 tiles (gx tiles per tile row, the
+// first at workgroup `first`).
+struct ColJob {
+    const uint16_t *x;
+    int64_t rows, cols, ld;
+    OutDesc out;
+    QKnobs kn;
+    int64_t first;
+    int64_t gx;
+    int32_t vec;
+    int32_t round;
+};
+constexpr int kColBatchMax = 8;
+struct ColBatch {
+    ColJob job[kColBatchMax];
+    int32_t n;
+};
+// Launch of the batched kernel: every job of b shares the grid family, the
+// rotation size hn and the column code format fmt; `tiles` = the jobs' total.
+hipError_t launch_quant_col_batch(int grid, int hn, int fmt, const ColBatch &b, int64_t tiles,
+                                  hipStream_t s);
+
 // Launch of the row-wise-only quantize kernel (two lanes per block).
 struct RowLaunch {
     const uint16_t *x;

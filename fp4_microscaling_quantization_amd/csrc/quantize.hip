@@ -94,13 +94,11 @@ QKnobs make_knobs(const mxq_qconfig *cfg)
     return kn;
 }
 
-}  // namespace mxq
+namespace {
 
-using namespace mxq;
-
-extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_t rows,
-                                   int64_t cols, int64_t ld_x, const mxq_qtensor *row_out,
-                                   const mxq_qtensor *col_out, void *stream)
+// The checks of mxq_quantize, in its documented order.
+mxq_status check_quantize(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
+                          int64_t ld_x, const mxq_qtensor *row_out, const mxq_qtensor *col_out)
 {
     mxq_status st = check_qconfig(cfg);
     if (st)
@@ -122,24 +120,42 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
     // grid-size limits of the launches (2^31 workgroups / 65535 row tiles)
     if (col_out && (rows + 127) / 128 > 65535)
         return MXQ_ERR_SHAPE;
+    return MXQ_OK;
+}
+
+OutDesc col_desc(const mxq_qtensor *col_out, int64_t rows, int64_t cols)
+{
+    return OutDesc{static_cast<uint8_t *>(col_out->codes), col_out->scales, col_out->fmt,
+                   col_out->layout, (uint64_t)(rows / 32), (uint64_t)((cols + 15) / 16)};
+}
+
+// kernels come in two grid families: E1M2, and E2M1 with or without a cap
+// (the cap and the scale exponent travel in the knobs)
+int grid_family(const mxq_qconfig *cfg) { return cfg->grid == MXQ_GRID_E1M2 ? kE1M2 : kE2M1; }
+
+// 8-byte loads of the column kernels when x and its rows are 8-byte aligned
+int col_vec(const void *x, int64_t ld_x)
+{
+    return (reinterpret_cast<uintptr_t>(x) % 8 == 0 && ld_x % 4 == 0) ? 1 : 0;
+}
+
+// The launches of one checked mxq_quantize call.
+mxq_status enqueue_quantize(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
+                            int64_t ld_x, const mxq_qtensor *row_out, const mxq_qtensor *col_out,
+                            hipStream_t s)
+{
     if (rows == 0 || cols == 0)
         return MXQ_OK;
-
     OutDesc rout{}, cout{};
     if (row_out)
         rout = OutDesc{static_cast<uint8_t *>(row_out->codes), row_out->scales, row_out->fmt,
                        row_out->layout, (uint64_t)(cols / 32), (uint64_t)((rows + 15) / 16)};
     if (col_out)
-        cout = OutDesc{static_cast<uint8_t *>(col_out->codes), col_out->scales, col_out->fmt,
-                       col_out->layout, (uint64_t)(rows / 32), (uint64_t)((cols + 15) / 16)};
+        cout = col_desc(col_out, rows, cols);
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     const uintptr_t xa = reinterpret_cast<uintptr_t>(x);
     const QKnobs kn = make_knobs(cfg);
-    hipStream_t s = static_cast<hipStream_t>(stream);
-
-    // kernels come in two grid families: E1M2, and E2M1 with or without a cap
-    // (the cap and the scale exponent travel in the knobs)
-    const int fam = cfg->grid == MXQ_GRID_E1M2 ? kE1M2 : kE2M1;
+    const int fam = grid_family(cfg);
     hipError_t e;
     if (!col_out) {
         // blocks along the contiguous dimension: 16-byte loads when aligned
@@ -149,7 +165,7 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
         e = launch_quant_row16(fam, cfg->round, cfg->hadamard_n, r);
     } else {
         // blocks along rows (alone or with the row output): 8-byte loads when aligned
-        const int vec8 = (xa % 8 == 0 && ld_x % 4 == 0) ? 1 : 0;
+        const int vec8 = col_vec(x, ld_x);
         if (!row_out) {
             ColLaunch c{xx, rows, cols, ld_x, cout, vec8, kn, s};
             e = launch_quant_col(fam, cfg->round, cfg->hadamard_n, c);
@@ -159,6 +175,99 @@ extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_
         }
     }
     return e == hipSuccess ? MXQ_OK : MXQ_ERR_DEVICE;
+}
+
+// 128 x 128 tiles of a column job
+int64_t col_tiles(const mxq_quantize_job &j) { return ((j.cols + 127) / 128) * ((j.rows + 127) / 128); }
+
+// the most workgroups one 1-D launch of 256-lane workgroups may have
+constexpr int64_t kMaxBatchTiles = (int64_t)0xFFFFFFFF / 256;
+
+// Jobs that the batched column kernel can share a launch with: a column
+// output only, something to do, and few enough tiles for a 1-D launch.
+bool col_only(const mxq_quantize_job &j)
+{
+    return !j.row_out && j.col_out && j.rows > 0 && j.cols > 0 && col_tiles(j) <= kMaxBatchTiles;
+}
+
+bool same_col_kernel(const mxq_quantize_job &a, const mxq_quantize_job &b)
+{
+    return grid_family(a.cfg) == grid_family(b.cfg) && a.cfg->hadamard_n == b.cfg->hadamard_n &&
+           a.col_out->fmt == b.col_out->fmt;
+}
+
+}  // namespace
+
+}  // namespace mxq
+
+using namespace mxq;
+
+extern "C" mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_t rows,
+                                   int64_t cols, int64_t ld_x, const mxq_qtensor *row_out,
+                                   const mxq_qtensor *col_out, void *stream)
+{
+    const mxq_status st = check_quantize(cfg, x, rows, cols, ld_x, row_out, col_out);
+    if (st)
+        return st;
+    return enqueue_quantize(cfg, x, rows, cols, ld_x, row_out, col_out,
+                            static_cast<hipStream_t>(stream));
+}
+
+extern "C" mxq_status mxq_quantize_batch(const mxq_quantize_job *jobs, int32_t count, void *stream)
+{
+    if (count < 0)
+        return MXQ_ERR_SHAPE;
+    if (count == 0)
+        return MXQ_OK;
+    if (!jobs)
+        return MXQ_ERR_NULL;
+    for (int32_t i = 0; i < count; ++i) {
+        const mxq_quantize_job &j = jobs[i];
+        const mxq_status st =
+            check_quantize(j.cfg, j.x, j.rows, j.cols, j.ld_x, j.row_out, j.col_out);
+        if (st)
+            return st;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    for (int32_t i = 0; i < count;) {
+        const mxq_quantize_job &j0 = jobs[i];
+        if (!col_only(j0)) {
+            const mxq_status st = enqueue_quantize(j0.cfg, j0.x, j0.rows, j0.cols, j0.ld_x,
+                                                   j0.row_out, j0.col_out, s);
+            if (st)
+                return st;
+            ++i;
+            continue;
+        }
+        // a run of consecutive column-only jobs that share one kernel
+        ColBatch b{};
+        int64_t tiles = 0;
+        int32_t n = 0;
+        while (i + n < count && n < kColBatchMax && col_only(jobs[i + n]) &&
+               same_col_kernel(j0, jobs[i + n]) && tiles + col_tiles(jobs[i + n]) <= kMaxBatchTiles) {
+            const mxq_quantize_job &j = jobs[i + n];
+            ColJob &q = b.job[n];
+            q.x = static_cast<const uint16_t *>(j.x);
+            q.rows = j.rows;
+            q.cols = j.cols;
+            q.ld = j.ld_x;
+            q.out = col_desc(j.col_out, j.rows, j.cols);
+            q.kn = make_knobs(j.cfg);
+            q.first = tiles;
+            q.gx = (j.cols + 127) / 128;
+            q.vec = col_vec(j.x, j.ld_x);
+            q.round = j.cfg->round == MXQ_ROUND_SR ? kSR : kRTNE;
+            tiles += col_tiles(j);
+            ++n;
+        }
+        b.n = n;
+        const hipError_t e = launch_quant_col_batch(grid_family(j0.cfg), j0.cfg->hadamard_n,
+                                                    j0.col_out->fmt, b, tiles, s);
+        if (e != hipSuccess)
+            return MXQ_ERR_DEVICE;
+        i += n;
+    }
+    return MXQ_OK;
 }
 
 extern "C" mxq_status mxq_round_to_grid(int32_t grid, int32_t round, int32_t sr_bits,

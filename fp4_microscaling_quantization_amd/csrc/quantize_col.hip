@@ -272,25 +272,27 @@ __device__ __forceinline__ void flush_stage(const OutDesc &o, const uint32_t *st
     }
 }
 
+// One 128 x 128 tile of the column-wise quantization: columns 128 bx ..,
+// rows 128 by .. (rows % 32 == 0).  `stage` is the workgroup's LDS image of
+// the tile's output (128 * BB words).
 template <int GRID, int ROUND, int HN, int FMT>
-__global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ x, int64_t rows,
-                                                   int64_t cols, int64_t ld, OutDesc out, int vec,
-                                                   QKnobs kn)
+__device__ __forceinline__ void col_tile(int64_t bx, int64_t by, const uint16_t *__restrict__ x,
+                                         int64_t rows, int64_t cols, int64_t ld,
+                                         const OutDesc &out, int vec, const QKnobs &kn,
+                                         uint32_t *stage)
 {
     const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
     const int pos = lane & 1, cg = lane >> 1;
-    const int64_t rband = (int64_t)blockIdx.y * 128 + wv * 32;  // rows % 32 == 0
+    const int64_t rband = by * 128 + wv * 32;  // rows % 32 == 0
     // A full 128 x 128 tile stages its codes in LDS and writes them as long
     // runs (MFMA layout: one run; row layout: 4 blocks per column).  Every wave
     // of such a workgroup has rows, so none returns early.
     constexpr int BB = FMT == MXQ_FMT_E2M3 ? 24 : 16;           // bytes per block
-    __shared__ uint32_t stage[128 * BB];                         // 128 columns x 4 blocks
-    const bool staged = (int64_t)blockIdx.x * 128 + 128 <= cols &&
-                        (int64_t)blockIdx.y * 128 + 128 <= rows;
+    const bool staged = bx * 128 + 128 <= cols && by * 128 + 128 <= rows;
     if (rband >= rows)
         return;                                                   // whole wave
     const int64_t r0 = rband + 16 * pos;
-    const int64_t c0 = (int64_t)blockIdx.x * 128 + 4 * cg;
+    const int64_t c0 = bx * 128 + 4 * cg;
     const uint64_t jb = (uint64_t)rband >> 5, nbc = (uint64_t)rows >> 5;
 
     // lo[i]: columns c0, c0 + 1 of row r0 + i; hi[i]: columns c0 + 2, c0 + 3
@@ -389,8 +391,66 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
     }
     if (staged) {
         __syncthreads();
-        flush_stage<BB>(out, stage, t, (uint64_t)blockIdx.x * 128, (uint64_t)blockIdx.y * 4);
+        flush_stage<BB>(out, stage, t, (uint64_t)bx * 128, (uint64_t)by * 4);
     }
+}
+
+template <int GRID, int ROUND, int HN, int FMT>
+__global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ x, int64_t rows,
+                                                   int64_t cols, int64_t ld, OutDesc out, int vec,
+                                                   QKnobs kn)
+{
+    __shared__ uint32_t stage[128 * (FMT == MXQ_FMT_E2M3 ? 24 : 16)];  // 128 columns x 4 blocks
+    col_tile<GRID, ROUND, HN, FMT>(blockIdx.x, blockIdx.y, x, rows, cols, ld, out, vec, kn, stage);
+}
+
+// Several column-wise quantizations in one launch (same grid family, rotation
+// and code format; each job its own rounding): workgroup w takes tile
+// w - first of the job whose tile range holds w, in the same x-fastest tile
+// order as k_quant_col's 2-D grid.  Jobs run in the order given, so a
+// compute-heavy job (SR) placed first lets the next job's tiles fill the
+// last partial wave of workgroups, and the launch gap between them goes.
+// The job's fields in SGPRs, read by a few wide scalar loads at the start.
+// Left to itself the compiler loads each field where it is first used, and
+// every such load's wait then stalls the waves in the middle of the tile.
+__device__ __forceinline__ ColJob load_job(const ColJob &src)
+{
+    constexpr int N = (int)(sizeof(ColJob) / 4);
+    const uint32_t *s = reinterpret_cast<const uint32_t *>(&src);
+    uint32_t v[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        v[i] = s[i];
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        asm volatile("" : "+s"(v[i]));
+    ColJob q;
+    uint32_t *d = reinterpret_cast<uint32_t *>(&q);
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+        d[i] = v[i];
+    return q;
+}
+
+template <int GRID, int HN, int FMT>
+__global__ __launch_bounds__(256) void k_quant_col_batch(ColBatch b)
+{
+    __shared__ uint32_t stage[128 * (FMT == MXQ_FMT_E2M3 ? 24 : 16)];
+    // the host keeps a launch below 2^24 workgroups: tile indices fit 32 bits
+    const uint32_t w = blockIdx.x;
+    int j = 0;
+#pragma unroll
+    for (int i = 1; i < kColBatchMax; ++i)
+        if (i < b.n && w >= (uint32_t)b.job[i].first)
+            j = i;
+    const ColJob q = load_job(b.job[j]);
+    const uint32_t tile = w - (uint32_t)q.first, gx = (uint32_t)q.gx;
+    const uint32_t by = tile / gx, bx = tile - by * gx;
+    if (q.round == kSR)
+        col_tile<GRID, kSR, HN, FMT>(bx, by, q.x, q.rows, q.cols, q.ld, q.out, q.vec, q.kn, stage);
+    else
+        col_tile<GRID, kRTNE, HN, FMT>(bx, by, q.x, q.rows, q.cols, q.ld, q.out, q.vec, q.kn,
+                                       stage);
 }
 
 // Row-wise fused rotate + quantize with the column kernel's per-lane work:
@@ -763,7 +823,38 @@ void launch_col_hn(int hn, const ColLaunch &q)
     }
 }
 
+template <int GRID, int HN>
+void launch_col_batch_fmt(int fmt, const ColBatch &b, int64_t tiles, hipStream_t s)
+{
+    if (fmt == MXQ_FMT_E2M3)
+        hipLaunchKernelGGL((k_quant_col_batch<GRID, HN, MXQ_FMT_E2M3>), dim3((unsigned)tiles),
+                           dim3(256), 0, s, b);
+    else
+        hipLaunchKernelGGL((k_quant_col_batch<GRID, HN, MXQ_FMT_FP4>), dim3((unsigned)tiles),
+                           dim3(256), 0, s, b);
+}
+
+template <int GRID>
+void launch_col_batch_hn(int hn, int fmt, const ColBatch &b, int64_t tiles, hipStream_t s)
+{
+    switch (hn) {
+    case 0: launch_col_batch_fmt<GRID, 0>(fmt, b, tiles, s); break;
+    case 16: launch_col_batch_fmt<GRID, 16>(fmt, b, tiles, s); break;
+    default: launch_col_batch_fmt<GRID, 32>(fmt, b, tiles, s); break;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quant_col_batch(int grid, int hn, int fmt, const ColBatch &b, int64_t tiles,
+                                  hipStream_t s)
+{
+    if (grid == kE2M1)
+        launch_col_batch_hn<kE2M1>(hn, fmt, b, tiles, s);
+    else
+        launch_col_batch_hn<kE1M2>(hn, fmt, b, tiles, s);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_dual16(int grid, int round, int hn, const DualLaunch &q)
 {

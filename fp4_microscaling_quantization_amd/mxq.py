@@ -22,7 +22,7 @@ AXIS_ROW, AXIS_COL = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
 SIGNS_MASK, SIGNS_PER_BLOCK = 0, 1
 
-SYMBOLS = ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "mxq_bias_stats",
+SYMBOLS = ("mxq_quantize", "mxq_quantize_batch", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "mxq_bias_stats",
            "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_rht_sign_mask", "mxq_rotate",
            "mxq_status_string", "mxq_abi_version")
 
@@ -37,6 +37,12 @@ class QConfig(C.Structure):
 class QTensor(C.Structure):
     _fields_ = [("codes", C.c_void_p), ("scales", C.c_void_p), ("fmt", C.c_int32),
                 ("grid", C.c_int32), ("layout", C.c_int32)]
+
+
+class QuantizeJob(C.Structure):
+    _fields_ = [("cfg", C.POINTER(QConfig)), ("x", C.c_void_p), ("rows", C.c_int64),
+                ("cols", C.c_int64), ("ld_x", C.c_int64), ("row_out", C.POINTER(QTensor)),
+                ("col_out", C.POINTER(QTensor))]
 
 
 class Stats(C.Structure):
@@ -66,6 +72,7 @@ def lib() -> C.CDLL:
         P, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         L.mxq_quantize.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, C.POINTER(QTensor),
                                    C.POINTER(QTensor), P]
+        L.mxq_quantize_batch.argtypes = [C.POINTER(QuantizeJob), i32, P]
         L.mxq_dequantize.argtypes = [C.POINTER(QTensor), i64, i64, i32, P, i64, P]
         L.mxq_wgrad_gemm.argtypes = [C.POINTER(QTensor), C.POINTER(QTensor), i64, i64, i64, P,
                                      i64, P]
@@ -81,7 +88,7 @@ def lib() -> C.CDLL:
         L.mxq_status_string.argtypes = [i32]
         L.mxq_status_string.restype = C.c_char_p
         L.mxq_abi_version.restype = i32
-        for name in ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt",
+        for name in ("mxq_quantize", "mxq_quantize_batch", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt",
                      "mxq_bias_stats", "mxq_round_to_grid", "mxq_rotate"):
             getattr(L, name).restype = i32
         _lib = L
@@ -192,6 +199,56 @@ def prepare_quantize(cfg: QConfig, x, row=None, col=None, stream=None):
 
     def call():
         _check("mxq_quantize", fn(*args))
+    call._keep = keep
+    return call
+
+
+def _addr(t) -> int:
+    """Device address of t; an empty view keeps the address of its storage
+    (torch reports 0 for tensors without elements)."""
+    p = t.data_ptr()
+    if p == 0 and t.numel() == 0:
+        p = t.untyped_storage().data_ptr() + t.storage_offset() * t.element_size()
+    return p
+
+
+def _batch_args(jobs):
+    """ctypes array of QuantizeJob for [(cfg, x, row, col), ...] (row / col as
+    in quantize_into) and the objects it points into."""
+    arr = (QuantizeJob * len(jobs))()
+    keep = [arr]
+    for i, (cfg, x, row, col) in enumerate(jobs):
+        cfg_ = QConfig.from_buffer_copy(cfg)
+
+        def desc(o):
+            if not o:
+                return None
+            lay = o[3] if len(o) > 3 else LAYOUT_ROWS
+            return QTensor(o[0].data_ptr(), o[1].data_ptr(), o[2], cfg_.grid, lay)
+        rt, ct = desc(row), desc(col)
+        keep += [cfg_, rt, ct]
+        arr[i] = QuantizeJob(C.pointer(cfg_), _addr(x), x.shape[0], x.shape[1], x.stride(0),
+                             C.pointer(rt) if rt else None, C.pointer(ct) if ct else None)
+    return arr, keep
+
+
+def quantize_batch(jobs, stream=None):
+    """mxq_quantize_batch: jobs = [(cfg, x, row, col), ...] with row / col
+    (codes, scales, fmt[, layout]) or None, as quantize_into."""
+    arr, keep = _batch_args(jobs)
+    st = lib().mxq_quantize_batch(arr, len(jobs), _stream(stream))
+    del keep
+    _check("mxq_quantize_batch", st)
+
+
+def prepare_quantize_batch(jobs, stream=None):
+    """quantize_batch(jobs) marshalled once (see prepare_quantize)."""
+    arr, keep = _batch_args(jobs)
+    args = (arr, len(jobs), _stream(stream))
+    fn = lib().mxq_quantize_batch
+
+    def call():
+        _check("mxq_quantize_batch", fn(*args))
     call._keep = keep
     return call
 

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 2
+#define MXQ_ABI_VERSION 3
 
 typedef int32_t mxq_status;
 #define MXQ_OK 0
@@ -198,6 +198,31 @@ typedef struct {
 mxq_status mxq_quantize(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
                         int64_t ld_x, const mxq_qtensor *row_out, const mxq_qtensor *col_out,
                         void *stream);
+
+/* One tensor of mxq_quantize_batch: the arguments of one mxq_quantize call. */
+typedef struct {
+    const mxq_qconfig *cfg;
+    const void *x;
+    int64_t rows, cols, ld_x;
+    const mxq_qtensor *row_out;  /* may be NULL */
+    const mxq_qtensor *col_out;  /* may be NULL */
+} mxq_quantize_job;
+
+/* mxq_quantize for `count` tensors at once, e.g. the two operands of the
+ * weight-gradient product, dY with SR and X with RTNE (htx.com news,
+ * "Experimento de diagnostico").  The outputs are bit-identical to calling
+ * mxq_quantize on each job in turn.  Every job is checked first, with
+ * mxq_quantize's checks and status codes; on the first failure nothing is
+ * launched and that status is returned.  Consecutive jobs that ask for a
+ * column output only and share the grid family (E1M2, or the E2M1 grids),
+ * hadamard_n and the column code format run as ONE launch (up to 8 jobs per
+ * launch), their workgroups in job order; the rounding mode, seeds, signs,
+ * shapes and layouts may differ.  Other jobs get their own launches, in
+ * order.  No output may overlap another job's output or input (inputs may
+ * be shared).  count == 0 does nothing; count < 0 -> MXQ_ERR_SHAPE; NULL
+ * jobs with count > 0 -> MXQ_ERR_NULL.  A launch failure returns
+ * MXQ_ERR_DEVICE; the launches before it stay enqueued. */
+mxq_status mxq_quantize_batch(const mxq_quantize_job *jobs, int32_t count, void *stream);
 
 /* Reconstruct yhat = (-1)^s G_m 2^(scale-127) (NaN for scale 0xFF) of a
  * block-quantized tensor into out [lines x k] (leading dimension ld_out

@@ -18,7 +18,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for want in ("mxq_quantize", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_bias_stats",
+    for want in ("mxq_quantize", "mxq_quantize_batch", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_bias_stats",
                  "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_status_string",
                  "mxq_abi_version"):
         assert want in names
@@ -35,7 +35,7 @@ def test_abi_version_and_status_strings(mxq_lib):
     L = mxq_lib.lib()
     import re
     hdr = open(os.path.join(ROOT, "include", "mxq.h")).read()
-    assert L.mxq_abi_version() == int(re.search(r"#define MXQ_ABI_VERSION (\d+)", hdr).group(1)) == 2
+    assert L.mxq_abi_version() == int(re.search(r"#define MXQ_ABI_VERSION (\d+)", hdr).group(1)) == 3
     for s in range(7):
         assert mxq_lib.status_string(s)
     assert mxq_lib.status_string(0) == "ok"
@@ -80,6 +80,41 @@ def test_quantize_validation(mxq_lib):
     # empty inputs are valid and launch nothing
     assert q(good, rows=0) == M.OK
     assert q(good, cols=0, ld=0) == M.OK
+
+
+def test_quantize_batch_validation(mxq_lib):
+    # every job is checked before anything is launched; the first failing
+    # job's status comes back, with mxq_quantize's codes
+    L = mxq_lib.lib()
+    M = mxq_lib
+    good, sr = M.qconfig(), M.qconfig(round=M.SR, grid=M.GRID_E1M2)
+    out = M.QTensor(0x20000, 0x30000, M.FMT_FP4, M.GRID_E2M1)
+    out1 = M.QTensor(0x24000, 0x34000, M.FMT_FP4, M.GRID_E1M2)
+    keep = [good, sr, out, out1]
+
+    def job(cfg=good, x=0x10000, rows=64, cols=64, ld=64, row=None, col=out):
+        return M.QuantizeJob(C.pointer(cfg) if cfg is not None else None, x, rows, cols, ld,
+                             C.pointer(row) if row is not None else None,
+                             C.pointer(col) if col is not None else None)
+
+    def b(*jobs, count=None):
+        arr = (M.QuantizeJob * max(len(jobs), 1))(*jobs)
+        return L.mxq_quantize_batch(arr, len(jobs) if count is None else count, None)
+
+    assert L.mxq_quantize_batch(None, 0, None) == M.OK
+    assert L.mxq_quantize_batch(None, 2, None) == M.ERR_NULL
+    assert b(job(), count=-1) == M.ERR_SHAPE
+    # the bad job is the last one: the good ones before it are not launched
+    assert b(job(), job(cfg=sr, col=out1), job(cfg=None)) == M.ERR_NULL
+    assert b(job(), job(x=None)) == M.ERR_NULL
+    assert b(job(), job(rows=48)) == M.ERR_SHAPE          # column blocks need rows % 32
+    assert b(job(), job(col=None, row=None)) == M.ERR_NULL
+    assert b(job(), job(cfg=sr, col=out)) == M.ERR_UNSUPPORTED   # output grid != cfg grid
+    assert b(job(), job(x=0x10001)) == M.ERR_ALIGN
+    assert b(job(), job(cfg=M.qconfig(hadamard_n=8))) == M.ERR_UNSUPPORTED
+    # jobs with nothing to do are valid and launch nothing
+    assert b(job(rows=0), job(cols=0, ld=0), job(cfg=sr, col=out1, rows=0)) == M.OK
+    del keep
 
 
 def test_gemm_validation(mxq_lib):
