@@ -39,6 +39,7 @@ struct ColJob {
     int32_t round;
 };
 constexpr int kColBatchMax = 8;
+constexpr int kBatchMixed = 2;  // a batch launch with both SR and RTNE jobs
 struct ColBatch {
     ColJob job[kColBatchMax];
     int32_t n;

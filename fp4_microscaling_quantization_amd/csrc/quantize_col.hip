@@ -432,7 +432,10 @@ __device__ __forceinline__ ColJob load_job(const ColJob &src)
     return q;
 }
 
-template <int GRID, int HN, int FMT>
+// RMODE: kRTNE or kSR when every job of the launch rounds that way (one
+// tile body, so the kernel keeps that body's register budget and occupancy),
+// kBatchMixed when both occur.
+template <int GRID, int HN, int FMT, int RMODE>
 __global__ __launch_bounds__(256) void k_quant_col_batch(ColBatch b)
 {
     __shared__ uint32_t stage[128 * (FMT == MXQ_FMT_E2M3 ? 24 : 16)];
@@ -446,7 +449,10 @@ __global__ __launch_bounds__(256) void k_quant_col_batch(ColBatch b)
     const ColJob q = load_job(b.job[j]);
     const uint32_t tile = w - (uint32_t)q.first, gx = (uint32_t)q.gx;
     const uint32_t by = tile / gx, bx = tile - by * gx;
-    if (q.round == kSR)
+    if constexpr (RMODE != kBatchMixed)
+        col_tile<GRID, RMODE, HN, FMT>(bx, by, q.x, q.rows, q.cols, q.ld, q.out, q.vec, q.kn,
+                                       stage);
+    else if (q.round == kSR)
         col_tile<GRID, kSR, HN, FMT>(bx, by, q.x, q.rows, q.cols, q.ld, q.out, q.vec, q.kn, stage);
     else
         col_tile<GRID, kRTNE, HN, FMT>(bx, by, q.x, q.rows, q.cols, q.ld, q.out, q.vec, q.kn,
@@ -823,24 +829,36 @@ void launch_col_hn(int hn, const ColLaunch &q)
     }
 }
 
+template <int GRID, int HN, int FMT>
+void launch_col_batch_rmode(int rmode, const ColBatch &b, int64_t tiles, hipStream_t s)
+{
+    const dim3 grid((unsigned)tiles);
+    if (rmode == kRTNE)
+        hipLaunchKernelGGL((k_quant_col_batch<GRID, HN, FMT, kRTNE>), grid, dim3(256), 0, s, b);
+    else if (rmode == kSR)
+        hipLaunchKernelGGL((k_quant_col_batch<GRID, HN, FMT, kSR>), grid, dim3(256), 0, s, b);
+    else
+        hipLaunchKernelGGL((k_quant_col_batch<GRID, HN, FMT, kBatchMixed>), grid, dim3(256), 0,
+                           s, b);
+}
+
 template <int GRID, int HN>
-void launch_col_batch_fmt(int fmt, const ColBatch &b, int64_t tiles, hipStream_t s)
+void launch_col_batch_fmt(int fmt, int rmode, const ColBatch &b, int64_t tiles, hipStream_t s)
 {
     if (fmt == MXQ_FMT_E2M3)
-        hipLaunchKernelGGL((k_quant_col_batch<GRID, HN, MXQ_FMT_E2M3>), dim3((unsigned)tiles),
-                           dim3(256), 0, s, b);
+        launch_col_batch_rmode<GRID, HN, MXQ_FMT_E2M3>(rmode, b, tiles, s);
     else
-        hipLaunchKernelGGL((k_quant_col_batch<GRID, HN, MXQ_FMT_FP4>), dim3((unsigned)tiles),
-                           dim3(256), 0, s, b);
+        launch_col_batch_rmode<GRID, HN, MXQ_FMT_FP4>(rmode, b, tiles, s);
 }
 
 template <int GRID>
-void launch_col_batch_hn(int hn, int fmt, const ColBatch &b, int64_t tiles, hipStream_t s)
+void launch_col_batch_hn(int hn, int fmt, int rmode, const ColBatch &b, int64_t tiles,
+                         hipStream_t s)
 {
     switch (hn) {
-    case 0: launch_col_batch_fmt<GRID, 0>(fmt, b, tiles, s); break;
-    case 16: launch_col_batch_fmt<GRID, 16>(fmt, b, tiles, s); break;
-    default: launch_col_batch_fmt<GRID, 32>(fmt, b, tiles, s); break;
+    case 0: launch_col_batch_fmt<GRID, 0>(fmt, rmode, b, tiles, s); break;
+    case 16: launch_col_batch_fmt<GRID, 16>(fmt, rmode, b, tiles, s); break;
+    default: launch_col_batch_fmt<GRID, 32>(fmt, rmode, b, tiles, s); break;
     }
 }
 
@@ -849,10 +867,14 @@ void launch_col_batch_hn(int hn, int fmt, const ColBatch &b, int64_t tiles, hipS
 hipError_t launch_quant_col_batch(int grid, int hn, int fmt, const ColBatch &b, int64_t tiles,
                                   hipStream_t s)
 {
+    bool sr = false, rtne = false;
+    for (int i = 0; i < b.n; ++i)
+        (b.job[i].round == kSR ? sr : rtne) = true;
+    const int rmode = sr && rtne ? kBatchMixed : sr ? kSR : kRTNE;
     if (grid == kE2M1)
-        launch_col_batch_hn<kE2M1>(hn, fmt, b, tiles, s);
+        launch_col_batch_hn<kE2M1>(hn, fmt, rmode, b, tiles, s);
     else
-        launch_col_batch_hn<kE1M2>(hn, fmt, b, tiles, s);
+        launch_col_batch_hn<kE1M2>(hn, fmt, rmode, b, tiles, s);
     return hipGetLastError();
 }
 

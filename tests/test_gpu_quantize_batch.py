@@ -85,9 +85,10 @@ def _check_job(orc, j, out, tag):
         assert np.array_equal(gc, c), (tag, key, "codes", np.argwhere(gc != c)[:5])
 
 
-def _col_jobs(grid_family, n, fmt, count, seed0):
-    """`count` column-only jobs of one kernel: ragged shapes, both roundings,
-    both sign modes, both layouts where the shape allows the MFMA one."""
+def _col_jobs(grid_family, n, fmt, count, seed0, rnd=None):
+    """`count` column-only jobs of one kernel: ragged shapes, both roundings
+    (or only `rnd`), both sign modes, both layouts where the shape allows the
+    MFMA one."""
     shapes = [(256, 100), (160, 72), (96, 130), (128, 256), (32, 8), (384, 40), (64, 129),
               (512, 16), (224, 200)]
     grids = [0, 2, 3] if grid_family == 0 else [1]
@@ -95,7 +96,8 @@ def _col_jobs(grid_family, n, fmt, count, seed0):
     for i in range(count):
         rows, cols = shapes[i % len(shapes)]
         x = synth.laplace_outlier_entries(rows, cols, seed=seed0 + i, out_seed=i, frac=0.01)
-        knobs = _knobs(grids[i % len(grids)], i % 2, n, seed0 + i, sign_mode=(i // 2) % 2)
+        knobs = _knobs(grids[i % len(grids)], i % 2 if rnd is None else rnd, n, seed0 + i,
+                       sign_mode=(i // 2) % 2)
         lay = 1 if rows % 128 == 0 and i % 3 != 2 else 0
         jobs.append(Job(x, knobs, col=(fmt, lay)))
     return jobs
@@ -106,6 +108,17 @@ def _col_jobs(grid_family, n, fmt, count, seed0):
 def test_one_launch_batch_parity(orc, family, n, fmt):
     jobs = _col_jobs(family, n, fmt, 5, seed0=10 * n + fmt + family)
     say("batch one launch", family, n, fmt, [j.x.shape for j in jobs])
+    outs = _run_batch(jobs)
+    for i, (j, o) in enumerate(zip(jobs, outs)):
+        _check_job(orc, j, o, f"job {i}")
+
+
+@pytest.mark.parametrize("rnd", [0, 1], ids=["rtne", "sr"])
+@pytest.mark.parametrize("family,n,fmt", [(1, 16, 1), (0, 32, 0)])
+def test_one_rounding_batch_parity(orc, family, n, fmt, rnd):
+    # every job rounds the same way: the launch takes the one-body kernel
+    jobs = _col_jobs(family, n, fmt, 4, seed0=40 + rnd, rnd=rnd)
+    say("batch one rounding", family, n, fmt, rnd)
     outs = _run_batch(jobs)
     for i, (j, o) in enumerate(zip(jobs, outs)):
         _check_job(orc, j, o, f"job {i}")
