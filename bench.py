@@ -152,6 +152,8 @@ def parse():
                     help="skip the fused / standalone / unfused quantize comparison")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the device-copy rate and the vendor-library GEMM reference")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the timing of each workload's quantize call")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -320,6 +322,9 @@ def main():
 
     if not args.no_context:
         rec["context"] = context_report(torch, dev, kernels)
+
+    if not args.no_workloads:
+        rec["workloads"] = workloads_report(torch, mxq, synth, dev, max(args.steps, 10))
 
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -569,6 +574,49 @@ def fusion_ratios(torch, mxq, synth, dev, reps):
                      "fused_over_standalone": round(tf / tp, 3),
                      "unfused_over_fused": round(tu / tf, 3)}
         del sets, fused, plain, unfused
+        torch.cuda.empty_cache()
+    return out
+
+
+def workloads_report(torch, mxq, synth, dev, reps):
+    """Every full-size quantize call of the five workloads (the parity tests'
+    cases: the 1024 x 1024 activation, the 8192 x 4096 activation with both
+    grids, the 14336 x 4096 weight with both outputs and both grids, the
+    16384 x 4096 gradient with SR, and the two Wgrad operands) in its own
+    back-to-back loop over two input/output sets: average launch time and
+    algorithmic bandwidth (2 B read per element; per output 0.5 or 0.75 B of
+    codes plus 1/32 B of scale per element)."""
+    import numpy as np
+    out = {}
+    s = torch.cuda.current_stream()
+    for case in synth.workload_cases():
+        x_np = case.make()
+        rows, cols = x_np.shape
+        cfg = mxq.qconfig(**case.knobs())
+        calls = []
+        for _ in range(2):
+            x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+            r = mxq.empty_qtensor(rows, cols, case.fmt, dev) if case.row_out else None
+            c = mxq.empty_qtensor(cols, rows, case.fmt, dev) if case.col_out else None
+            calls.append(mxq.prepare_quantize(cfg, x, row=(r[0], r[1], case.fmt) if r else None,
+                                              col=(c[0], c[1], case.fmt) if c else None))
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        time.sleep(0.05)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(s)
+        for i in range(reps):
+            calls[i % 2]()
+        e1.record(s)
+        torch.cuda.synchronize()
+        t = e0.elapsed_ms(e1) * 1e-3 / reps
+        nout = int(case.row_out) + int(case.col_out)
+        out_bytes = quant_bytes_per_elem(case.fmt) - 2.0     # codes + scale per element
+        nbytes = rows * cols * (2.0 + nout * out_bytes)
+        out[case.name] = {"avg_us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+                          "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del calls
         torch.cuda.empty_cache()
     return out
 
