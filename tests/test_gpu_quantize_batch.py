@@ -143,10 +143,22 @@ def test_mixed_batch_parity(orc):
         _check_job(orc, j, o, f"job {i}")
 
 
+def _mfma_tile(codes, scales, t, lines, k, fmt):
+    """Bytes of 16-line tile t of an MFMA-layout tensor [lines x k], as the
+    layout of a 16-line tensor: codes [steps][64 lanes][bb], scales [groups][64][4]."""
+    bb = 16 if fmt == 0 else 24
+    ntiles, steps = (lines + 15) // 16, k // 128
+    c = codes.reshape(steps, ntiles, 64 * bb)[:, t, :].reshape(-1)
+    s = scales.reshape((steps + 3) // 4, ntiles, 256)[:, t, :].reshape(-1)
+    return c, s
+
+
 def test_wgrad_pair_full_size(orc):
     """The weight-gradient step's two operands in one launch, as the benchmark
-    runs them: byte-equal to two mxq_quantize calls, and 8-column slices at
-    both ends and in the middle of each output equal the oracle."""
+    runs them: byte-equal to two mxq_quantize calls; in the benchmark's
+    matrix-core layout, 16-column tiles at both ends and in the middle of each
+    output equal the oracle's quantization of those columns placed by the
+    oracle's layout; in the row layout, 8-column slices equal the oracle."""
     from fp4_microscaling_quantization_amd import mxq
     import torch
     cases = [c for c in synth.workload_cases() if c.name.startswith("wgrad_")]
@@ -169,7 +181,17 @@ def test_wgrad_pair_full_size(orc):
         torch.cuda.synchronize()
         for (_, _, _, b), (_, _, s) in zip(batch, single):
             assert torch.equal(b[0], s[0]) and torch.equal(b[1], s[1]), lay
-        if lay != mxq.LAYOUT_ROWS:
+        if lay == mxq.LAYOUT_MFMA:
+            for c, x, (_, _, _, b) in zip(cases, hx, batch):
+                p = orc.qparams(**c.knobs())
+                rows, cols = x.shape
+                gc, gs = host(b[0]), host(b[1])
+                for t in (0, cols // 32, cols // 16 - 1):
+                    oc, os_ = orc.quantize_lines(x, orc.AXIS_COL, p, 16 * t, 16, c.fmt)
+                    tc, ts = orc.to_mfma_layout(oc, os_, c.fmt)
+                    wc, ws = _mfma_tile(gc, gs, t, cols, rows, c.fmt)
+                    assert np.array_equal(ws, ts), (c.name, "tile", t, "scales")
+                    assert np.array_equal(wc, tc), (c.name, "tile", t, "codes")
             continue
         for c, x, (_, _, _, b) in zip(cases, hx, batch):
             p = orc.qparams(**c.knobs())
