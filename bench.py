@@ -152,6 +152,8 @@ def parse():
                     help="skip the fused / standalone / unfused quantize comparison")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the device-copy rate and the vendor-library GEMM reference")
+    ap.add_argument("--no-layer-gemms", action="store_true",
+                    help="skip the Fprop / Dgrad GEMM timings")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the timing of each workload's quantize call")
     ap.add_argument("--copy-calib", action="store_true",
@@ -325,6 +327,10 @@ def main():
 
     if not args.no_workloads:
         rec["workloads"] = workloads_report(torch, mxq, synth, dev, max(args.steps, 10))
+
+    if not args.no_layer_gemms:
+        rec["layer_gemms"] = layer_gemms_report(torch, mxq, synth, dev, grid, fmt,
+                                                max(args.steps, 10), mfma_peak)
 
     if args.copy_calib:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -617,6 +623,53 @@ def workloads_report(torch, mxq, synth, dev, reps):
         out[case.name] = {"avg_us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
                           "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
         del calls
+        torch.cuda.empty_cache()
+    return out
+
+
+def layer_gemms_report(torch, mxq, synth, dev, grid, fmt, reps, peak):
+    """The other two GEMMs of the MLP up-projection (8192 tokens, K = 4096,
+    N = 14336) through mxq_gemm_abt, with operands in the matrix-core layout
+    as the layer GEMM parity tests build them: Fprop Y = X W^T (m = 8192,
+    n = 14336, k = 4096) and Dgrad dX = dY W (m = 8192, n = 4096, k = 14336).
+    Each product runs `reps` times back to back over two output buffers."""
+    import numpy as np
+    T_, K_, N_ = 8192, 4096, 14336
+    lay = mxq.LAYOUT_MFMA
+
+    def to_dev(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    signs = synth.sign_mask(synth.SIGNS_W, 32)
+    kw = dict(grid=grid, round=mxq.RTNE, hadamard_n=32, sign_mask=signs)
+    kd = dict(grid=grid, round=mxq.SR, hadamard_n=32, sign_mask=signs, sr_seed=11)
+    qx = mxq.quantize(to_dev(synth.x_8192x4096()), row=True, col=False, row_fmt=fmt,
+                      row_layout=lay, **kw)["row"]
+    qw = mxq.quantize(to_dev(synth.w_14336x4096()), row=True, col=True, row_fmt=fmt,
+                      col_fmt=fmt, row_layout=lay, col_layout=lay, **kw)
+    qd = mxq.quantize(to_dev(synth.dy_8192x14336()), row=True, col=False, row_fmt=fmt,
+                      row_layout=lay, **kd)["row"]
+    out = {}
+    s = torch.cuda.current_stream()
+    for name, a, b, m, n, k in (("fprop", qx, qw["row"], T_, N_, K_),
+                                ("dgrad", qd, qw["col"], T_, K_, N_)):
+        cs = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
+        calls = [mxq.prepare_wgrad_gemm(a[0], a[1], fmt, grid, b[0], b[1], fmt, grid, c, lay,
+                                        m, n, k, entry="mxq_gemm_abt") for c in cs]
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        time.sleep(0.05)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(s)
+        for i in range(reps):
+            calls[i % 2]()
+        e1.record(s)
+        torch.cuda.synchronize()
+        t = e0.elapsed_ms(e1) * 1e-3 / reps
+        tf = 2.0 * m * n * k / t / 1e12
+        out[name] = {"m": m, "n": n, "k": k, "avg_us": round(t * 1e6, 2),
+                     "TFLOP_s": round(tf, 1), "frac": round(tf / peak, 4)}
+        del cs, calls
         torch.cuda.empty_cache()
     return out
 

@@ -308,15 +308,16 @@ def wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_gri
 
 
 def prepare_wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid, out,
-                       layout, m, n, k, stream=None):
-    """wgrad_gemm(...) marshalled once into a function of no arguments."""
+                       layout, m, n, k, stream=None, entry="mxq_wgrad_gemm"):
+    """wgrad_gemm(...) marshalled once into a function of no arguments
+    (entry="mxq_gemm_abt" for the same product under its general name)."""
     qa = qtensor(a_codes, a_scales, a_fmt, a_grid, layout)
     qb = qtensor(b_codes, b_scales, b_fmt, b_grid, layout)
     args = (C.byref(qa), C.byref(qb), m, n, k, _ptr(out), out.stride(0), _stream(stream))
-    fn = lib().mxq_wgrad_gemm
+    fn = getattr(lib(), entry)
 
     def call():
-        _check("mxq_wgrad_gemm", fn(*args))
+        _check(entry, fn(*args))
     call._keep = (qa, qb)
     return call
 

@@ -93,12 +93,14 @@ class QuantCase:
     sr_seed: int = 0
     sr_stream: int = 0
     sr_bits: int = 16
+    sign_mode: int = 0                # 0: one mask for every block; 1: drawn per block
+    sign_seed: int = 0
     extra: dict = field(default_factory=dict)
 
     def knobs(self) -> dict:
         return dict(grid=self.grid, round=self.round, hadamard_n=self.hadamard_n,
                     sign_mask=self.sign_mask, sr_seed=self.sr_seed, sr_stream=self.sr_stream,
-                    sr_bits=self.sr_bits)
+                    sr_bits=self.sr_bits, sign_mode=self.sign_mode, sign_seed=self.sign_seed)
 
 
 # --- the five workloads ------------------------------------------------------
@@ -146,7 +148,8 @@ SR_SEED_WGRAD = 7
 
 
 def workload_cases() -> list[QuantCase]:
-    """The quantize calls of the five workloads, at full size."""
+    """The quantize calls of the five workloads at full size, plus the
+    range-restricted E2M1 grid and per-block signs on the same tensors."""
     return [
         QuantCase("x1024_e2m1_rtne", 1024, 1024, x_1024),
         QuantCase("x8192_h16_e2m1", 8192, 4096, x_8192x4096, hadamard_n=16),
@@ -155,6 +158,11 @@ def workload_cases() -> list[QuantCase]:
                   sign_mask=sign_mask(SIGNS_W, 32), col_out=True),
         QuantCase("w14336_rht32_e1m2_dual", 14336, 4096, w_14336x4096, grid=GRID_E1M2,
                   hadamard_n=32, sign_mask=sign_mask(SIGNS_W, 32), col_out=True),
+        # the range-restricted E2M1 grid and per-block random signs on the same tensors
+        QuantCase("x8192_h16_e2m1max4", 8192, 4096, x_8192x4096, grid=GRID_E2M1_MAX4,
+                  hadamard_n=16),
+        QuantCase("w14336_rht32_e2m1_dual_signs_per_block", 14336, 4096, w_14336x4096,
+                  hadamard_n=32, col_out=True, sign_mode=1, sign_seed=SIGNS_W),
         QuantCase("dy16384_rht16_e1m2_sr_col", 16384, 4096, dy_16384x4096, grid=GRID_E1M2,
                   round=SR, hadamard_n=16, sign_mask=sign_mask(SIGNS_DY, 16), row_out=False,
                   col_out=True, sr_seed=0),
