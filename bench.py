@@ -51,12 +51,12 @@ KERNEL_SOURCES = {
 }
 MEASURED_TRAFFIC = {
     "e1m2": {
-        "quantize_pair_col": {"read": 134639021, "write": 52433527, "sha": "7a97cd3972432c31"},
-        "wgrad_gemm": {"read": 157553886, "write": 67170953, "sha": "89476f4b16a9b7b1"},
+        "quantize_pair_col": {"read": 134635098, "write": 52429275, "sha": "9a53d9b56c197dc3"},
+        "wgrad_gemm": {"read": 157553404, "write": 67112969, "sha": "89476f4b16a9b7b1"},
     },
     "e2m1": {
-        "quantize_pair_col": {"read": 134685033, "write": 35656375, "sha": "7a97cd3972432c31"},
-        "wgrad_gemm": {"read": 107207245, "write": 67114176, "sha": "89476f4b16a9b7b1"},
+        "quantize_pair_col": {"read": 134688292, "write": 35652599, "sha": "9a53d9b56c197dc3"},
+        "wgrad_gemm": {"read": 107206488, "write": 67116087, "sha": "89476f4b16a9b7b1"},
     },
 }
 
@@ -206,15 +206,15 @@ def main():
 
     # the launches of each set, marshalled once so that the host stays ahead
     # of the GPU and the events time the kernels, not the launch path.  A step
-    # is one batched quantize launch of both operands (dY's SR tiles first,
-    # then X's RTNE tiles) and the GEMM; the two separate quantize launches
-    # are timed as well, for comparison.
+    # is one batched quantize launch of both operands (X's RTNE tiles first,
+    # then dY's SR tiles: 1-2% faster than the other order) and the GEMM; the
+    # two separate quantize launches are timed as well, for comparison.
     calls = []
     for dy, xx, qd, qx, c in sets:
         col_dy = (qd[0], qd[1], fmt, mxq.LAYOUT_MFMA)
         col_x = (qx[0], qx[1], fmt, mxq.LAYOUT_MFMA)
         calls.append((
-            mxq.prepare_quantize_batch([(cfg_dy, dy, None, col_dy), (cfg_x, xx, None, col_x)]),
+            mxq.prepare_quantize_batch([(cfg_x, xx, None, col_x), (cfg_dy, dy, None, col_dy)]),
             mxq.prepare_wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, c,
                                    mxq.LAYOUT_MFMA, N, K, T),
             mxq.prepare_quantize(cfg_dy, dy, col=col_dy),

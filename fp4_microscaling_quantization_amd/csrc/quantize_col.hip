@@ -407,9 +407,9 @@ __global__ __launch_bounds__(256) void k_quant_col(const uint16_t *__restrict__ 
 // Several column-wise quantizations in one launch (same grid family, rotation
 // and code format; each job its own rounding): workgroup w takes tile
 // w - first of the job whose tile range holds w, in the same x-fastest tile
-// order as k_quant_col's 2-D grid.  Jobs run in the order given, so a
-// compute-heavy job (SR) placed first lets the next job's tiles fill the
-// last partial wave of workgroups, and the launch gap between them goes.
+// order as k_quant_col's 2-D grid.  Jobs run in the order given: the next
+// job's tiles fill the last partial wave of the previous job's workgroups,
+// and the launch gap between separate kernels goes.
 // The job's fields in SGPRs, read by a few wide scalar loads at the start.
 // Left to itself the compiler loads each field where it is first used, and
 // every such load's wait then stalls the waves in the middle of the tile.
