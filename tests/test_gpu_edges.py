@@ -85,3 +85,31 @@ def test_largest_column_launch(orc):
     with pytest.raises(mxq.MxqError) as e:
         mxq.quantize(too_many, row=False, col=True, **kw)
     assert e.value.status == mxq.ERR_SHAPE
+
+
+def test_largest_column_launch_in_a_batch(orc):
+    # the same largest column job batched with a small one: one 1-D launch of
+    # 65535 + 1 tiles, the small job's tiles after the large one's
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    rows, cols = 65535 * 128, 32
+    x = synth.laplace_outlier_entries(rows, cols, seed=45, out_seed=46, frac=1e-4)
+    y = synth.normal(128, 96, seed=47)
+    kw = dict(grid=mxq.GRID_E1M2, round=mxq.SR, hadamard_n=16, sign_mask=synth.sign_mask(48, 16),
+              sr_seed=49)
+    ky = dict(kw, round=mxq.RTNE)
+    say("largest column launch, batched", rows, cols)
+    xt, yt = to_dev_bf16(x), to_dev_bf16(y)
+    qx = mxq.empty_qtensor(cols, rows, mxq.FMT_E2M3, xt.device)
+    qy = mxq.empty_qtensor(96, 128, mxq.FMT_E2M3, yt.device)
+    mxq.quantize_batch([(mxq.qconfig(**kw), xt, None, (qx[0], qx[1], mxq.FMT_E2M3)),
+                        (mxq.qconfig(**ky), yt, None, (qy[0], qy[1], mxq.FMT_E2M3))])
+    torch.cuda.synchronize()
+    gc, gs = host(qx[0]), host(qx[1])
+    p = orc.qparams(**kw)
+    for line in (0, 17, 31):
+        c, s = orc.quantize_lines(x, orc.AXIS_COL, p, line, 1, orc.FMT_E2M3)
+        assert np.array_equal(gs[line], s[0]), line
+        assert np.array_equal(gc[line], c[0]), line
+    c, s = orc.quantize(y, orc.AXIS_COL, orc.qparams(**ky), orc.FMT_E2M3)
+    assert np.array_equal(host(qy[1]), s) and np.array_equal(host(qy[0]), c)
