@@ -95,7 +95,8 @@ constexpr float level_unit()
 // (bf16 widened, random signs applied).  Rotates, finds the block's E8M0
 // code (returned) and leaves in v the rounded levels times level_unit(), with
 // the sign of the rotated value (for E2M1 with RTNE and FP4 output, the
-// unrounded value times 2: the FP4 convert rounds it).
+// unrounded value times 2: the FP4 convert rounds it; for E1M2 with FP4
+// output, the bits of the sign-magnitude nibble).
 template <int GRID, int ROUND, int HN, bool EXACT_LEVEL>
 __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk, const QKnobs &kn,
                                           float h, float h2)
@@ -163,7 +164,15 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
             const float t = v[i] * m2;  // 2 a, signed
             if constexpr (GRID == kE1M2) {
                 // levels 0.5 m: m = RNE(2a), saturated at 7
-                v[i] = rintf(__builtin_amdgcn_fmed3f(t, -7.0f, 7.0f));
+                const float c = __builtin_amdgcn_fmed3f(t, -7.0f, 7.0f);
+                if constexpr (EXACT_LEVEL)
+                    v[i] = rintf(c);
+                else  // the FP4 nibble: RNE(|c|) is the low bits of 2^23 + |c|, and
+                      // bit 3 of as_u(c) >> 28 (nothing above it) is c's sign;
+                      // one bitop3 selects bits 0-2 from the first, the rest from
+                      // the second (truth table 0xE4: s2 ? s0 : s1)
+                    v[i] = as_f(__builtin_amdgcn_bitop3_b32(as_u(fabsf(c) + 8388608.0f),
+                                                            as_u(c) >> 28, 7u, 0xE4));
             } else if constexpr (!EXACT_LEVEL) {
                 // the FP4 convert rounds t / 2 to nearest even (saturating at 6);
                 // a capped grid stops at its cap first
@@ -185,7 +194,12 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
             if constexpr (GRID == kE1M2) {
                 // x = min(2a, 7) - h; level index ceil(x - 2 h r)
                 const float x = fminf(__builtin_fmaf(fabsf(v[i]), m2, -h), 7.0f - h);
-                v[i] = copysignf(ceilf(__builtin_fmaf(rf[i], -h2, x)), v[i]);
+                const float m = ceilf(__builtin_fmaf(rf[i], -h2, x));
+                if constexpr (EXACT_LEVEL)
+                    v[i] = copysignf(m, v[i]);
+                else  // the FP4 nibble, as for RTNE (m is an integer 0..7)
+                    v[i] = as_f(__builtin_amdgcn_bitop3_b32(as_u(m + 8388608.0f),
+                                                            as_u(v[i]) >> 28, 7u, 0xE4));
             } else {
                 // a in units of the local step (S / 4 for 2a below 2 S): x = 2a * 2 / S
                 const float a2 = fminf(fabsf(v[i]) * m2, kn.top2);
@@ -213,10 +227,8 @@ __device__ __forceinline__ void pack_fp4(const float (&v)[16], uint32_t sc, uint
             x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[8 * d + 6], v[8 * d + 7], u, 3);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float q = v[8 * d + i];  // the level index m, signed
-                x |= ((uint32_t)fabsf(q) | ((as_u(q) >> 28) & 8u)) << (4 * i);
-            }
+            for (int i = 0; i < 8; ++i)
+                x |= as_u(v[8 * d + i]) << (4 * i);  // col16 left the nibble itself
         }
         w[d] = sc == 0xFFu ? 0u : x;
     }
