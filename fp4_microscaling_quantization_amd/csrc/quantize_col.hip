@@ -59,29 +59,19 @@ __device__ __forceinline__ void cvt_e2m3_32(const f16v &a, const f16v &b, float 
         out[i] = r[i];
 }
 
-// Random values of the lane's 16 positions 16 pos + i as fp32 integers:
-// element j = 16 pos + i of block `blk` takes Philox4x32-10 on counter
-// (j >> 3, blk lo, blk hi, stream), half j & 1 of word (j >> 1) & 3 for
-// 16-bit draws; counter (j >> 4, ...), byte j & 3 of word (j >> 2) & 3 for
-// 8-bit draws (the definition in include/mxq.h).
-__device__ __forceinline__ void sr_rand16(const QKnobs &kn, int pos, uint64_t blk, float (&rf)[16])
+// Philox4x32-10 output for the lane's positions 16 pos + 8 g .. + 7 with
+// 16-bit draws: element j of block `blk` takes counter (j >> 3, blk lo,
+// blk hi, stream), half j & 1 of word (j >> 1) & 3; with 8-bit draws
+// (g = 0 only) element j takes counter (j >> 4, ...), byte j & 3 of word
+// (j >> 2) & 3 (the definition in include/mxq.h).  The draws stay packed
+// in the four output words until their position is rounded: sixteen fp32
+// copies held at once would push the SR tile body past 128 VGPRs (three
+// waves per SIMD instead of four).
+__device__ __forceinline__ Rand4 sr_draw(const QKnobs &kn, int pos, int g, uint64_t blk)
 {
-    const uint32_t blo = (uint32_t)blk, bhi = (uint32_t)(blk >> 32);
-    if (kn.sr_bits == 16) {
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const Rand4 q = philox4x32_10((uint32_t)(2 * pos + half), blo, bhi, kn.stream,
-                                          kn.seed_lo, kn.seed_hi);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                rf[8 * half + i] = (float)((q.w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-        }
-    } else {
-        const Rand4 q = philox4x32_10((uint32_t)pos, blo, bhi, kn.stream, kn.seed_lo, kn.seed_hi);
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            rf[i] = (float)((q.w[i >> 2] >> (8 * (i & 3))) & 0xFFu);
-    }
+    const uint32_t ctr = kn.sr_bits == 16 ? (uint32_t)(2 * pos + g) : (uint32_t)pos;
+    return philox4x32_10(ctr, (uint32_t)blk, (uint32_t)(blk >> 32), kn.stream, kn.seed_lo,
+                         kn.seed_hi);
 }
 
 // The convert scale that maps the values col16 leaves behind onto the grid.
@@ -187,14 +177,12 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
             }
         }
     } else {
-        float rf[16];
-        sr_rand16(kn, pos, blk, rf);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        // round position i with its random integer r (as fp32)
+        auto sr_one = [&](int i, float r) {
             if constexpr (GRID == kE1M2) {
                 // x = min(2a, 7) - h; level index ceil(x - 2 h r)
                 const float x = fminf(__builtin_fmaf(fabsf(v[i]), m2, -h), 7.0f - h);
-                const float m = ceilf(__builtin_fmaf(rf[i], -h2, x));
+                const float m = ceilf(__builtin_fmaf(r, -h2, x));
                 if constexpr (EXACT_LEVEL)
                     v[i] = copysignf(m, v[i]);
                 else  // the FP4 nibble, as for RTNE (m is an integer 0..7)
@@ -205,8 +193,20 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
                 const float a2 = fminf(fabsf(v[i]) * m2, kn.top2);
                 const float S = as_f(max(as_u(a2) & 0x7F800000u, 0x40000000u));
                 const float x = __builtin_fmaf(a2, as_f(0x7F800000u - as_u(S)), -h);
-                v[i] = copysignf(ceilf(__builtin_fmaf(rf[i], -h2, x)) * S, v[i]);
+                v[i] = copysignf(ceilf(__builtin_fmaf(r, -h2, x)) * S, v[i]);
             }
+        };
+        if (kn.sr_bits == 16) {
+            // both draws first: two independent Philox chains interleave
+            const Rand4 q[2] = {sr_draw(kn, pos, 0, blk), sr_draw(kn, pos, 1, blk)};
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                sr_one(i, (float)((q[i >> 3].w[(i >> 1) & 3] >> (16 * (i & 1))) & 0xFFFFu));
+        } else {
+            const Rand4 q = sr_draw(kn, pos, 0, blk);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                sr_one(i, (float)((q.w[i >> 2] >> (8 * (i & 3))) & 0xFFu));
         }
     }
     return sc;
