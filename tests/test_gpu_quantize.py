@@ -132,6 +132,8 @@ def test_sr_8_bit_stream(orc):
         p = _params(orc, grid, 1, 16, seed=8, sr_bits=8)
         _check(orc, x, p, row_fmt=0, tag="sr8-row")
         _check(orc, x, p, col_fmt=0, tag="sr8-col")
+        _check(orc, x, p, col_fmt=1, tag="sr8-col-e2m3")
+        _check(orc, x, p, row_fmt=1, col_fmt=0, tag="sr8-dual")
 
 
 def test_repeatable_bitwise(orc):
