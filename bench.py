@@ -15,7 +15,11 @@ last-level cache.
 Timing: W untimed warmup steps; then the timed region, K whole steps back to
 back between two HIP events (ms_per_step); then each kernel K times back to
 back between two events (after a 50 ms idle gap), which gives its average
-launch duration without event records between launches.
+launch duration without event records between launches; then, for the batched
+quantize and the GEMM, 100 launches with an event recorded after each, whose
+intervals give the median, p10 and p90 per launch (`distribution`; each
+interval also holds its event's own time, so the median sits above the loop
+average).
 
 The JSON line reports the fused quantize bandwidth as `value` (algorithmic
 bytes of both operands / the average duration of the one batched launch that
@@ -76,6 +80,23 @@ def measured_traffic(variant: str, kernel: str):
     if m is None or m["sha"] != source_sha(kernel):
         return None
     return m["read"] + m["write"]
+
+
+def launch_percentiles(us: list) -> dict:
+    """Median, p10 and p90 (linear interpolation between order statistics) of
+    per-launch durations in microseconds."""
+    xs = sorted(us)
+    if not xs:
+        raise ValueError("no launches")
+
+    def q(p):
+        h = (len(xs) - 1) * p
+        lo = int(h)
+        hi = min(lo + 1, len(xs) - 1)
+        return xs[lo] + (xs[hi] - xs[lo]) * (h - lo)
+
+    return {"median_us": round(q(0.5), 3), "p10_us": round(q(0.1), 3),
+            "p90_us": round(q(0.9), 3), "launches": len(xs)}
 
 
 def quant_bytes_per_elem(fmt: int) -> float:
@@ -156,6 +177,8 @@ def parse():
                     help="skip the Fprop / Dgrad GEMM timings")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the timing of each workload's quantize call")
+    ap.add_argument("--dist-launches", type=int, default=100,
+                    help="launches per kernel for the per-launch duration distribution (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -255,6 +278,20 @@ def main():
         return timed(lambda i: calls[i % len(calls)][j](), args.steps) / args.steps
     t_qp, t_gm, t_qdy, t_qx = (own_loop(j) for j in range(4))
 
+    # per-launch durations: n launches of one kernel back to back over the
+    # rotating sets, an event recorded after each (events that take no system
+    # fence, so the launches stay back to back); duration i = event i to i + 1
+    def per_launch(j, n):
+        evs = [HipEvent() for _ in range(n + 1)]
+        time.sleep(0.05)
+        torch.cuda.synchronize()
+        evs[0].record(stream)
+        for i in range(n):
+            calls[i % len(calls)][j]()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        return launch_percentiles([evs[i].elapsed_ms(evs[i + 1]) * 1e3 for i in range(n)])
+
     elems = T * N
     qbytes = elems * quant_bytes_per_elem(fmt)                           # per operand
     flops = 2.0 * N * K * T
@@ -315,6 +352,12 @@ def main():
         "roofline": dom,
         "kernels": kernels,
     }
+
+    if args.dist_launches > 0:
+        rec["distribution"] = {"quantize_pair_col": per_launch(0, args.dist_launches),
+                               "wgrad_gemm": per_launch(1, args.dist_launches),
+                               "note": "event-to-event interval per launch, an event recorded "
+                                       "after each; includes the event's own time"}
 
     if not args.no_quality:
         rec["quality"] = quality_report(torch, mxq, synth, dev)

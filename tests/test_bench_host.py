@@ -1,6 +1,6 @@
 """CPU checks of bench.py's host logic: the one-GPU guard, the algorithmic
-byte counts, and the rule that measured HBM traffic is reported only for the
-kernel sources it was measured on."""
+byte counts, the per-launch percentiles, and the rule that measured HBM traffic
+is reported only for the kernel sources it was measured on."""
 import os
 import subprocess
 import sys
@@ -39,3 +39,16 @@ def test_traffic_only_for_the_measured_sources(monkeypatch):
             assert bench.measured_traffic(variant, name) is None
             monkeypatch.setitem(bench.MEASURED_TRAFFIC, variant, kernels)
     assert bench.measured_traffic("e1m2", "no_such_kernel") is None
+
+
+def test_launch_percentiles():
+    import numpy as np
+    xs = [float(v) for v in np.random.default_rng(5).permutation(101)]   # 0 .. 100
+    d = bench.launch_percentiles(xs)
+    assert (d["median_us"], d["p10_us"], d["p90_us"], d["launches"]) == (50.0, 10.0, 90.0, 101)
+    # interpolation agrees with numpy's default (linear) percentile
+    ys = list(np.random.default_rng(6).exponential(40.0, 37))
+    d = bench.launch_percentiles(ys)
+    for key, p in (("median_us", 50), ("p10_us", 10), ("p90_us", 90)):
+        assert abs(d[key] - round(float(np.percentile(ys, p)), 3)) < 1e-9
+    assert bench.launch_percentiles([7.0])["median_us"] == 7.0
