@@ -25,7 +25,9 @@ The JSON line reports the fused quantize bandwidth as `value` (algorithmic
 bytes of both operands / the average duration of the one batched launch that
 quantizes them), the GEMM
 rate under `gemm`, the roofline of the dominant kernel and of each kernel,
-and the CPU oracle timed on a bounded sample as `cpu_baseline`.
+and the CPU oracle timed on a bounded sample as `cpu_baseline` (one thread;
+under `all_cores`, the same oracle on every host core this process may use, at
+most 16, over both whole operands).
 """
 import argparse
 import json
@@ -754,7 +756,7 @@ def cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, budget_s):
         g2 = min(g2, ncol)
         if g2 > 32:
             g, tg = g2, gemm(g2)
-    return {
+    rec = {
         "value": round(qbytes / tq / 1e9, 5),
         "unit": "GB/s",
         "cores": 1,
@@ -763,6 +765,74 @@ def cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, budget_s):
                   f"in {tq:.1f}s; fp64 GEMM of {g}x{g} outputs over K={T} in {tg:.1f}s",
         "gemm_tflops": round(2.0 * g * g * T / tg / 1e12, 6),
         "cpu": _cpu_model(),
+    }
+    rec["all_cores"] = cpu_baseline_threads(dy_np, x_np, pd, px, fmt, grid, tg / (2.0 * g * g * T))
+    return rec
+
+
+def oracle_threads() -> int:
+    """Host threads for the all-core oracle run: the CPUs this process may use,
+    at most 16 (one GPU's share of the host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def split_range(n: int, parts: int) -> list:
+    """[start, stop) bounds of `parts` near-equal consecutive pieces of range(n)."""
+    parts = max(1, min(parts, n)) if n > 0 else 1
+    q, r = divmod(n, parts)
+    out, a = [], 0
+    for i in range(parts):
+        b = a + q + (1 if i < r else 0)
+        out.append((a, b))
+        a = b
+    return out
+
+
+def cpu_baseline_threads(dy_np, x_np, pd, px, fmt, grid, s_per_flop):
+    """The same oracle on every core it may use: the column-wise quantization of
+    both whole operands, columns split over threads (each oracle call is one C
+    call, which releases the interpreter lock), and an fp64 GEMM sample split
+    over output rows, sized to about 3 s."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    from oracle import oracle as orc
+
+    nt = oracle_threads()
+    pieces = split_range(N, nt)
+    with ThreadPoolExecutor(max_workers=nt) as ex:
+        t0 = time.perf_counter()
+        res = list(ex.map(lambda ab: (orc.quantize_lines(dy_np, orc.AXIS_COL, pd, ab[0], ab[1] - ab[0], fmt),
+                                      orc.quantize_lines(x_np, orc.AXIS_COL, px, ab[0], ab[1] - ab[0], fmt)),
+                          pieces))
+        tq = time.perf_counter() - t0
+        cd = np.concatenate([r[0][0] for r in res])
+        sd = np.concatenate([r[0][1] for r in res])
+        cx = np.concatenate([r[1][0] for r in res])
+        sx = np.concatenate([r[1][1] for r in res])
+        # the GEMM sample: g x g outputs, g sized from the one-thread rate to ~3 s
+        g = int((3.0 * nt / max(s_per_flop, 1e-15) / (2.0 * T)) ** 0.5) // 32 * 32
+        g = max(32, min(g, N))
+        # the GEMM's operands, dequantized outside the timed region (also split)
+        rows = split_range(g, nt)
+        a = np.concatenate(list(ex.map(lambda ab: orc.dequantize(cd[ab[0]:ab[1]], sd[ab[0]:ab[1]], grid, fmt), rows)))
+        b = np.concatenate(list(ex.map(lambda ab: orc.dequantize(cx[ab[0]:ab[1]], sx[ab[0]:ab[1]], grid, fmt), rows)))
+        t1 = time.perf_counter()
+        list(ex.map(lambda ab: orc.gemm_abt_f64(a[ab[0]:ab[1]], b), rows))
+        tg = time.perf_counter() - t1
+    qbytes = 2 * N * T * quant_bytes_per_elem(fmt)
+    return {
+        "value": round(qbytes / tq / 1e9, 5),
+        "unit": "GB/s",
+        "cores": nt,
+        "sample": f"column-wise quantize of all {N} columns of dY and of X (T={T}) over {nt} "
+                  f"threads in {tq:.2f}s; fp64 GEMM of {g}x{g} outputs over K={T} in {tg:.1f}s",
+        "gemm_tflops": round(2.0 * g * g * T / tg / 1e12, 6),
     }
 
 

@@ -52,3 +52,27 @@ def test_launch_percentiles():
     for key, p in (("median_us", 50), ("p10_us", 10), ("p90_us", 90)):
         assert abs(d[key] - round(float(np.percentile(ys, p)), 3)) < 1e-9
     assert bench.launch_percentiles([7.0])["median_us"] == 7.0
+
+
+def test_split_range_covers_in_order():
+    for n, parts in ((4096, 16), (10, 3), (5, 8), (1, 1), (7, 1)):
+        r = bench.split_range(n, parts)
+        assert r[0][0] == 0 and r[-1][1] == n
+        assert all(a < b for a, b in r)
+        assert all(r[i][1] == r[i + 1][0] for i in range(len(r) - 1))
+        sizes = [b - a for a, b in r]
+        assert max(sizes) - min(sizes) <= 1
+    assert 1 <= bench.oracle_threads() <= 16
+
+
+def test_threaded_oracle_matches_one_call():
+    # the all-core baseline concatenates per-thread column ranges: same codes as one call
+    import numpy as np
+    from oracle import oracle as orc
+    from fp4_microscaling_quantization_amd import synth
+    x = synth.normal(64, 96, seed=11)
+    p = orc.qparams(grid=1, round=1, hadamard_n=16, sign_mask=0x5A5A, sr_seed=9)
+    whole = orc.quantize_lines(x, orc.AXIS_COL, p, 0, 96, 1)
+    parts = [orc.quantize_lines(x, orc.AXIS_COL, p, a, b - a, 1) for a, b in bench.split_range(96, 5)]
+    assert np.array_equal(np.concatenate([c for c, _ in parts]), whole[0])
+    assert np.array_equal(np.concatenate([s for _, s in parts]), whole[1])
