@@ -475,6 +475,152 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_tiled(const uint8_t *_
         }
 }
 
+// ---- 3-stage ring ------------------------------------------------------------
+// The product and tiling of k_wgrad_tiled, with each step's copies issued two
+// steps ahead into a 3-stage LDS ring.  A copy reaches LDS about a microsecond
+// after it is issued, longer than one step's products take, so with one step of
+// lead the waves wait on the copies at every barrier; two steps of lead hide
+// that.  Each step waits only for its own copies (vmcnt = the number of copies
+// issued since, i.e. those of the next step), so the next step's copies stay in
+// flight across the barrier.  That holds only while the loop has no other
+// vector-memory load outstanding: a compiler-generated wait for such a load
+// would also drain every copy issued after it.  So the scale words come through
+// LDS too: with a 4-step group's first step, the 16 A and 16 B tiles' scale
+// words of that group (2 x 4 KiB, one 1 KiB copy per wave) go into one of two
+// group buffers, and each lane reads its 12 words from there.
+template <int FA, int FB>
+constexpr int ring3_lds_bytes() { return 3 * 16 * 64 * (blk_bytes<FA>() + blk_bytes<FB>()) + 2 * 8192; }
+
+template <int FA, int FB>
+__global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *__restrict__ ac,
+                                                                const uint8_t *__restrict__ as,
+                                                                const uint8_t *__restrict__ bc,
+                                                                const uint8_t *__restrict__ bs,
+                                                                int64_t m, int64_t n, int64_t k,
+                                                                float *__restrict__ c, int64_t ldc)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int SA = 16 * 64 * blk_bytes<FA>(), SB = 16 * 64 * blk_bytes<FB>();
+    constexpr int STAGE = SA + SB;
+    constexpr int CA = SA / 1024, CB = SB / 1024;          // 1 KB chunks per operand
+    constexpr int PER = (CA + CB) / kWaves;                // chunks per wave per step
+    static_assert(PER * kWaves == CA + CB, "chunks split evenly over the waves");
+    static_assert(kWaves == 8, "one scale chunk per wave: 4 of A, 4 of B");
+    uint8_t *const scl = smem + 3 * STAGE;                 // 2 group buffers of 8 KiB
+
+    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    const int wm = wv >> 2, wn = wv & 3, g = lane >> 4, li = lane & 15;
+    int tm, tn;
+    tile_of(blockIdx.x, (int)((m + kBM - 1) / kBM), (int)((n + kBN - 1) / kBN), tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    const int64_t ntA = (m + 15) / 16, ntB = (n + 15) / 16;
+    const int64_t nsteps = k / 128;
+
+    // operand chunks, as in k_wgrad_tiled
+    constexpr int TBA = 64 * blk_bytes<FA>(), TBB = 64 * blk_bytes<FB>();
+    uint32_t goff[PER];
+    bool isA[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int ch = wv * PER + i;
+        isA[i] = ch < CA;
+        const int cc = isA[i] ? ch : ch - CA;
+        const int tb = isA[i] ? TBA : TBB;
+        const int o = cc * 1024 + lane * 16;
+        const int64_t tile = isA[i] ? min(m0 / 16 + o / TBA, ntA - 1) : min(n0 / 16 + o / TBB, ntB - 1);
+        goff[i] = (uint32_t)(tile * tb + o % tb);
+    }
+    // this wave's scale chunk of a group: wave w < 4 copies A tiles 4w .. 4w + 3
+    // of the workgroup's 16, wave w >= 4 B tiles 4 (w - 4) ..; lane L carries
+    // the words of lanes 4 (L % 16) .. + 3 of tile 4 (w % 4) + L / 16, so the
+    // buffer holds [A 16 tiles | B 16 tiles][64 lanes][4 B] (tiles past the
+    // operand's last are clamped, as for the codes)
+    const bool sIsA = wv < 4;
+    const int64_t stile = sIsA ? min(m0 / 16 + 4 * (wv & 3) + lane / 16, ntA - 1)
+                               : min(n0 / 16 + 4 * (wv & 3) + lane / 16, ntB - 1);
+    const uint8_t *const sbase = (sIsA ? as : bs) + stile * 256 + (lane & 15) * 16;
+    const int64_t sstride = (sIsA ? ntA : ntB) * 256;    // bytes per group
+
+    auto stage = [&](int64_t s, uint8_t *buf) {
+        const uint8_t *sa_ = ac + s * ntA * TBA, *sb_ = bc + s * ntB * TBB;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ch = wv * PER + i;
+            dma16((isA[i] ? sa_ : sb_) + goff[i], buf + (isA[i] ? ch * 1024 : SA + (ch - CA) * 1024));
+        }
+        if ((s & 3) == 0)
+            dma16(sbase + (s >> 2) * sstride, scl + ((s >> 2) & 1) * 8192 + wv * 1024);
+    };
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    stage(0, smem);
+    if (nsteps > 1)
+        stage(1, smem + STAGE);
+    uint32_t ca[8], cb[4];
+    int cur = 0, nxt2 = 2;                  // ring slots of steps s and s + 2
+    for (int64_t s = 0; s < nsteps; ++s) {
+        // this wave's copies for step s landed (those of step s + 1, issued
+        // after them, may still be in flight) ...
+        if (s + 1 >= nsteps)
+            wait_all_vm();
+        else if (((s + 1) & 3) == 0)
+            __builtin_amdgcn_s_waitcnt(0x0F70 | (PER + 1));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0F70 | PER);
+        barrier_no_fence();                 // ... and everyone's; step s-1's slot is free
+        if ((s & 3) == 0) {
+            const uint32_t *sg = reinterpret_cast<const uint32_t *>(scl + ((s >> 2) & 1) * 8192);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                ca[i] = sg[(8 * wm + i) * 64 + lane];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                cb[j] = sg[1024 + (4 * wn + j) * 64 + lane];
+        }
+        if (s + 2 < nsteps)
+            stage(s + 2, smem + nxt2 * STAGE);
+        const uint8_t *st = smem + cur * STAGE;
+        const int sh = 8 * (int)(s & 3);
+        v8i bf[4];
+        int sb[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bf[j] = tiled_fragment<FB>(st + SA, 4 * wn + j, lane);
+            sb[j] = (int)((cb[j] >> sh) & 0xFFu);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const v8i af = tiled_fragment<FA>(st, 8 * wm + i, lane);
+            const int sa = (int)((ca[i] >> sh) & 0xFFu);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af, bf[j], acc[i][j], FA, FB, 0, sa, 0, sb[j]);
+        }
+        cur = cur == 2 ? 0 : cur + 1;
+        nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
+    }
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + 64 * wn + 16 * j + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + 128 * wm + 16 * i + 4 * g + r;
+                if (row < m && col < n)
+                    c[row * ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
 __global__ __launch_bounds__(256) void k_zero_fill(float *__restrict__ c, int64_t m, int64_t n,
                                                    int64_t ldc)
 {
@@ -504,6 +650,18 @@ hipError_t launch_tiled(int64_t tiles, hipStream_t s, const uint8_t *ac, const u
                         const uint8_t *bc, const uint8_t *bs, int64_t m, int64_t n, int64_t k,
                         float *c, int64_t ldc)
 {
+    if (reinterpret_cast<uintptr_t>(as) % 16 == 0 && reinterpret_cast<uintptr_t>(bs) % 16 == 0) {
+        // scale words copied 16 bytes per lane: the 3-stage ring
+        constexpr int lds = ring3_lds_bytes<FA, FB>();
+        static const hipError_t attr = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&k_wgrad_ring3<FA, FB>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (attr != hipSuccess)
+            return attr;
+        hipLaunchKernelGGL((k_wgrad_ring3<FA, FB>), dim3((unsigned)tiles), dim3(64 * kWaves), lds,
+                           s, ac, as, bc, bs, m, n, k, c, ldc);
+        return hipGetLastError();
+    }
     constexpr int lds = tiled_lds_bytes<FA, FB>();
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&k_wgrad_tiled<FA, FB>),

@@ -238,6 +238,37 @@ def test_gemm_mfma_layout_random_scales(orc, combo):
     assert err <= 1e-6, err
 
 
+def _shifted(t, by=4):
+    """The same bytes at a device address `by` bytes past a 16-byte boundary."""
+    import torch
+    buf = torch.zeros(t.numel() + 16, dtype=torch.uint8, device=t.device)
+    v = buf[by:by + t.numel()]
+    v.copy_(t.reshape(-1))
+    assert v.data_ptr() % 16 == by
+    return v
+
+
+@pytest.mark.parametrize("shape", [(300, 520, 1152), (16, 16, 128)])
+@pytest.mark.parametrize("combo", COMBOS, ids=lambda c: f"A{c[0]}B{c[1]}")
+def test_gemm_mfma_layout_scales_not_16_byte_aligned(orc, shape, combo):
+    """Scale arrays on a 4- but not 16-byte boundary (what the interface allows)
+    take the kernel that reads scale words from global memory; the aligned case
+    copies them 16 bytes per lane.  Both give the exact product."""
+    from fp4_microscaling_quantization_amd import mxq
+    m, n, k = shape
+    (fa, ga), (fb, gb) = combo
+    g = np.random.Generator(np.random.PCG64(5 * m + n + k))
+    ac, as_ = _rand_codes(g, m, k, fa, ga, orc)
+    bc, bs = _rand_codes(g, n, k, fb, gb, orc)
+    say("gemm tiled, scales at +4 bytes", shape, combo)
+    ta, tas = _tiled(orc, ac, as_, fa)
+    tb, tbs = _tiled(orc, bc, bs, fb)
+    ref = orc.gemm_abt_f64(orc.dequantize(ac, as_, ga, fa), orc.dequantize(bc, bs, gb, fb))
+    for sa, sb in ((_shifted(tas), _shifted(tbs)), (tas, _shifted(tbs, 8))):
+        c = host(mxq.wgrad_gemm(ta, sa, fa, ga, tb, sb, fb, gb, layout=mxq.LAYOUT_MFMA, m=m, n=n, k=k))
+        assert np.array_equal(c.astype(np.float64), ref)
+
+
 @pytest.mark.parametrize("fmt,grid", [(0, 0), (1, 1)])
 def test_dequantize_mfma_layout(orc, fmt, grid):
     from fp4_microscaling_quantization_amd import mxq
