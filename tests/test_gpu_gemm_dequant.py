@@ -269,6 +269,25 @@ def test_gemm_mfma_layout_scales_not_16_byte_aligned(orc, shape, combo):
         assert np.array_equal(c.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("combo", COMBOS[:3], ids=lambda c: f"A{c[0]}B{c[1]}")
+def test_gemm_mfma_layout_same_bits_whatever_the_scale_alignment(orc, combo):
+    """Random scales (inexact fp32 sums): both kernels issue the same products in
+    the same order, so the result does not depend on where the scales sit."""
+    from fp4_microscaling_quantization_amd import mxq
+    m, n, k = 272, 528, 2560
+    (fa, ga), (fb, gb) = combo
+    g = np.random.Generator(np.random.PCG64(29))
+    ac, as_ = _rand_codes(g, m, k, fa, ga, orc, 100, 150)
+    bc, bs = _rand_codes(g, n, k, fb, gb, orc, 100, 150)
+    say("gemm tiled, scale alignment", combo)
+    ta, tas = _tiled(orc, ac, as_, fa)
+    tb, tbs = _tiled(orc, bc, bs, fb)
+    c1 = host(mxq.wgrad_gemm(ta, tas, fa, ga, tb, tbs, fb, gb, layout=mxq.LAYOUT_MFMA, m=m, n=n, k=k))
+    c2 = host(mxq.wgrad_gemm(ta, _shifted(tas), fa, ga, tb, _shifted(tbs, 12), fb, gb,
+                             layout=mxq.LAYOUT_MFMA, m=m, n=n, k=k))
+    assert np.array_equal(c1, c2)
+
+
 @pytest.mark.parametrize("fmt,grid", [(0, 0), (1, 1)])
 def test_dequantize_mfma_layout(orc, fmt, grid):
     from fp4_microscaling_quantization_amd import mxq
