@@ -314,6 +314,9 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_lds(const uint8_t *__restrict_
 // completion is awaited explicitly (vmcnt) before the barrier that publishes
 // the buffer.  A lane's 4 scale bytes per 4-step group come straight from
 // global memory, one dword per fragment row, a group ahead.
+// k_wgrad_tiled is that 2-stage form; it serves scale arrays that are not
+// 16-byte aligned.  Aligned ones take k_wgrad_ring3 below (3 stages, scale
+// words copied through LDS), which issues the same products in the same order.
 constexpr int kWaves = 8;
 
 __device__ __forceinline__ void dma16(const uint8_t *g, const uint8_t *l)
