@@ -27,7 +27,7 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     common = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-              "-Wall", "-Wno-unused-function"]
+              "-Wall", "-Wno-unused-function", "-Werror=inline-asm"]
     procs = []
     objs = []
     for src in sources():

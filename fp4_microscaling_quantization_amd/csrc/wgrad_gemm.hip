@@ -319,13 +319,25 @@ __global__ __launch_bounds__(256, 1) void k_wgrad_lds(const uint8_t *__restrict_
 // words copied through LDS), which issues the same products in the same order.
 constexpr int kWaves = 8;
 
+// M0 is a register the compiler reserves (it may hold a live value of its own
+// across this statement, e.g. for an LDS instruction it emitted), so the copy
+// saves it into an SGPR of its own, points it at the LDS destination, and puts
+// the saved value back before the statement ends.  The load takes M0 when it
+// is issued, so the restore right behind it does not change the copy.  The
+// build treats -Winline-asm as an error, so a reserved register can never sit
+// on a clobber list unnoticed.
 __device__ __forceinline__ void dma16(const uint8_t *g, const uint8_t *l)
 {
     const uint32_t la = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t *)l);
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %2\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
                  : "v"(g), "s"(__builtin_amdgcn_readfirstlane(la))
-                 : "memory", "m0");
+                 : "memory");
 }
 
 __device__ __forceinline__ void wait_all_vm()
