@@ -52,3 +52,18 @@ def special_matrix(rows: int, cols: int, seed: int) -> np.ndarray:
         bits[:, 3] = 0x8000
         bits[:, 5] = 0x0001
     return bits
+
+
+def check_product(got, ref, absref, k, what):
+    """A GEMM output against the fp64 product of the dequantized operands.
+    Each output sums k / 128 matrix-core steps of 128 products (four scaled
+    blocks of 32 per step) in fp32: at most 5 roundings per step, each moving
+    it by at most 2^-24 of the running sum of |a||b| (absref).  So every
+    element lies within 5 (k / 128) 2^-24 absref of the fp64 value, and the
+    relative Frobenius error must not exceed 1e-6."""
+    bound = 5 * (k // 128) * 2.0 ** -24 * absref
+    over = np.abs(got - ref) > bound
+    assert not over.any(), (what, int(over.sum()), np.argwhere(over)[:4].tolist())
+    err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    assert err <= 1e-6, (what, err)
+    return err

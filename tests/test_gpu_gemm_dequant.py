@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from fp4_microscaling_quantization_amd import synth
-from gpuhelp import dev, host, say, to_dev_bf16
+from gpuhelp import check_product, dev, host, say, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -303,11 +303,14 @@ def test_dequantize_mfma_layout(orc, fmt, grid):
 
 
 @pytest.mark.parametrize("variant", ["e1m2_e2m3", "e2m1_fp4"])
-def test_wgrad_step_full_size_mfma_layout(orc, variant):
-    """The benchmark's configuration: dY, X 8192 x 4096 quantized column-wise
-    straight into the matrix-core layout, then dW = dY^T X; 96 x 96 sampled
-    outputs against the oracle pipeline."""
-    import torch
+def test_wgrad_step_full_size_whole(orc, variant):
+    """The benchmark's step at full size and in its launch configuration: dY
+    and X 8192 x 4096 quantized by one batched launch (X with RTNE, then dY
+    with SR) straight into the matrix-core layout, then dW = dY^T X.  Every
+    operand byte is checked against the oracle's output placed by the
+    oracle's layout map, and every one of the 4096 x 4096 outputs against the
+    fp64 product of the oracle's dequantized operands."""
+    import oracle_par
     from fp4_microscaling_quantization_amd import mxq
     dy = synth.dy_8192x4096()
     xx = synth.x_wgrad_8192x4096()
@@ -315,21 +318,22 @@ def test_wgrad_step_full_size_mfma_layout(orc, variant):
     grid, fmt = (1, 1) if variant == "e1m2_e2m3" else (0, 0)
     kd = dict(grid=grid, round=1, hadamard_n=16, sign_mask=signs, sr_seed=synth.SR_SEED_WGRAD)
     kx = dict(grid=grid, round=0, hadamard_n=16, sign_mask=signs)
-    say("wgrad full tiled", variant)
-    qd = mxq.quantize(to_dev_bf16(dy), row=False, col=True, col_fmt=fmt,
-                      col_layout=mxq.LAYOUT_MFMA, **kd)["col"]
-    qx = mxq.quantize(to_dev_bf16(xx), row=False, col=True, col_fmt=fmt,
-                      col_layout=mxq.LAYOUT_MFMA, **kx)["col"]
+    say("wgrad full whole", variant)
+    qd = mxq.empty_qtensor(4096, 8192, fmt, dev(), mxq.LAYOUT_MFMA)
+    qx = mxq.empty_qtensor(4096, 8192, fmt, dev(), mxq.LAYOUT_MFMA)
+    mxq.quantize_batch([(mxq.qconfig(**kx), to_dev_bf16(xx), None, (qx[0], qx[1], fmt, mxq.LAYOUT_MFMA)),
+                        (mxq.qconfig(**kd), to_dev_bf16(dy), None, (qd[0], qd[1], fmt, mxq.LAYOUT_MFMA))])
     c = mxq.wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid,
                        layout=mxq.LAYOUT_MFMA, m=4096, n=4096, k=8192)
-    torch.cuda.synchronize()
-    g = np.random.Generator(np.random.PCG64(23))
-    I = np.sort(g.choice(4096, 96, replace=False))
-    J = np.sort(g.choice(4096, 96, replace=False))
-    pd, px = orc.qparams(**kd), orc.qparams(**kx)
-    A = np.concatenate([orc.dequantize(*orc.quantize_lines(dy, orc.AXIS_COL, pd, int(i), 1, fmt), grid, fmt) for i in I])
-    B = np.concatenate([orc.dequantize(*orc.quantize_lines(xx, orc.AXIS_COL, px, int(j), 1, fmt), grid, fmt) for j in J])
-    ref = orc.gemm_abt_f64(A, B)
-    got = c[torch.from_numpy(I).to(c.device)][:, torch.from_numpy(J).to(c.device)].cpu().numpy()
-    err = np.linalg.norm(got - ref) / np.linalg.norm(ref)
-    assert err <= 1e-6, err
+    got = host(c).astype(np.float64)
+    ops = []
+    for t, kn, q, name in ((dy, kd, qd, "dY"), (xx, kx, qx, "X")):
+        oc, os_ = oracle_par.quantize(orc, t, orc.AXIS_COL, orc.qparams(**kn), fmt)
+        tc, ts = orc.to_mfma_layout(oc, os_, fmt)
+        assert np.array_equal(host(q[1]), ts), (name, "scales")
+        assert np.array_equal(host(q[0]), tc), (name, "codes")
+        ops.append(oracle_par.dequantize(orc, oc, os_, grid, fmt))
+    A, B = ops
+    ref = oracle_par.gemm_abt_f64(orc, A, B)
+    absref = oracle_par.gemm_abt_f64(orc, np.abs(A), np.abs(B))
+    say("wgrad rel. Frobenius error", check_product(got, ref, absref, 8192, "dW"))
