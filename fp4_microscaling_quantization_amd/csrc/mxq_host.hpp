@@ -74,4 +74,14 @@ struct DualLaunch {
 };
 hipError_t launch_quant_dual16(int grid, int round, int hn, const DualLaunch &q);
 
+// Statistics (dequant_stats.hip): the argument checks of mxq_bias_stats other
+// than the workspace's, the workspace it needs, and the launch of its kernels
+// with the workgroup partials in `part`.
+mxq_status check_stats(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
+                       int64_t ld_x, int32_t axis, const mxq_qtensor *q, const mxq_stats *out);
+size_t stats_workspace_bytes(int64_t rows, int64_t cols, int32_t axis);
+mxq_status launch_stats(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
+                        int64_t ld_x, int32_t axis, const mxq_qtensor *q, mxq_stats *out,
+                        double *part, hipStream_t s);
+
 }  // namespace mxq

@@ -67,3 +67,33 @@ def check_product(got, ref, absref, k, what):
     err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
     assert err <= 1e-6, (what, err)
     return err
+
+
+def stats_close(st, ref, top_err=2.0):
+    """GPU statistics against the oracle's.  Counts must be equal.  The fp64
+    sums add the same per-element terms (each term is the same fp64
+    expression on both sides) in different orders: the GPU in per-lane sums,
+    then a fixed tree; the oracle in element order.  Recursive summation of n
+    terms in any order is within (n - 1) 2^-53 sum|t_i| of the exact sum, so
+    the two differ by at most 2 (n - 1) 2^-53 sum|t_i|, with sum|t_i| bounded
+    per sum: the sum itself for the non-negative ones (|y|, y^2, err^2),
+    sqrt(n sum err^2) for the signed error (Cauchy-Schwarz), and top_err per
+    element for the normalized errors |G_m - a| (at most 2, the largest
+    saturation error of E2M1: a < 8 rounded to 6)."""
+    for k in ("n", "n_saturated", "n_nonfinite_blocks", "level_count"):
+        assert st[k] == ref[k], k
+    n = max(ref["n"], 1)
+    tol = lambda absum, cnt: 2.0 * max(cnt - 1, 0) * 2.0 ** -53 * absum
+    bounds = {
+        "sum_abs_y": tol(ref["sum_abs_y"], n),
+        "sum_y2": tol(ref["sum_y2"], n),
+        "sum_err2": tol(ref["sum_err2"], n),
+        "sum_signed_err": tol(np.sqrt(n * ref["sum_err2"]), n),
+        "sum_err_norm": tol(top_err * n, n),
+        "sum_err_norm_sat": tol(top_err * ref["n_saturated"], ref["n_saturated"]),
+    }
+    for k, b in bounds.items():
+        assert abs(st[k] - ref[k]) <= b, (k, st[k], ref[k], b)
+    for m in range(8):
+        c = ref["level_count"][m]
+        assert abs(st["level_err_norm"][m] - ref["level_err_norm"][m]) <= tol(top_err * c, c), m

@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 from fp4_microscaling_quantization_amd import synth
-from gpuhelp import check_product, dev, host, say, to_dev_bf16
+from gpuhelp import check_product, dev, host, say, special_matrix, stats_close, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -155,12 +155,50 @@ def test_bias_stats_match_oracle(orc, axis, knobs):
     p = orc.qparams(**kw)
     oc, os_ = orc.quantize(x, axis, p, fmt)
     ref = orc.stats(x, axis, p, oc, os_, fmt)
-    for key_ in ("n", "n_saturated", "n_nonfinite_blocks", "level_count"):
-        assert st[key_] == ref[key_], key_
-    for key_ in ("sum_abs_y", "sum_signed_err", "sum_y2", "sum_err2", "sum_err_norm",
-                 "sum_err_norm_sat"):
-        assert np.isclose(st[key_], ref[key_], rtol=1e-12, atol=1e-300), key_
-    assert np.allclose(st["level_err_norm"], ref["level_err_norm"], rtol=1e-12, atol=1e-12)
+    stats_close(st, ref)
+
+
+@pytest.mark.parametrize("axis", [0, 1])
+@pytest.mark.parametrize("fmt", [0, 1])
+@pytest.mark.parametrize("ld", [None, 1540])
+def test_bias_stats_many_workgroups_special_values(orc, axis, fmt, ld):
+    """Statistics over 2048 x 1536 (hundreds of workgroups, several work items
+    per lane, ragged column runs, non-finite blocks), with a dense and a
+    padded leading dimension (the padded one takes the narrow loads)."""
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    rows, cols = 2048, 1536
+    x = special_matrix(rows, cols, seed=19)
+    kw = dict(grid=1 if fmt else 0, round=1, hadamard_n=16, sign_mask=synth.sign_mask(21, 16),
+              sr_seed=5)
+    say("stats large", axis, fmt, ld)
+    if ld is None:
+        xt = to_dev_bf16(x)
+    else:
+        wide = np.zeros((rows, ld), np.uint16)
+        wide[:, :cols] = x
+        xt = to_dev_bf16(wide)[:, :cols]
+    key = "row" if axis == 0 else "col"
+    q = mxq.quantize(xt, row=axis == 0, col=axis == 1, row_fmt=fmt, col_fmt=fmt, **kw)[key]
+    st = mxq.bias_stats(xt, axis, q[0], q[1], fmt, **kw)
+    again = mxq.bias_stats(xt, axis, q[0], q[1], fmt, **kw)
+    assert st == again                     # fixed-order reduction: repeatable bit for bit
+    p = orc.qparams(**kw)
+    oc, os_ = orc.quantize(x, axis, p, fmt)
+    assert np.array_equal(q[0].cpu().numpy(), oc) and np.array_equal(q[1].cpu().numpy(), os_)
+    ref = orc.stats(x, axis, p, oc, os_, fmt)
+    assert ref["n_nonfinite_blocks"] > 0
+    stats_close(st, ref)
+    # both sides against the exactly rounded sums of the oracle's rotated values
+    import math
+    y = orc.rotate(x, axis, kw["hadamard_n"], kw["sign_mask"]).astype(np.float64)
+    sc = os_.astype(np.int64).repeat(32, axis=1).reshape(y.shape)
+    fin = sc != 0xFF
+    yf = y[fin]
+    n = yf.size
+    for k, exact in (("sum_abs_y", math.fsum(np.abs(yf))), ("sum_y2", math.fsum(yf * yf))):
+        b = max(n - 1, 0) * 2.0 ** -53 * exact
+        assert abs(st[k] - exact) <= b and abs(ref[k] - exact) <= b, k
 
 
 def test_sr_unbiased_over_64_seeds(orc):
