@@ -172,4 +172,11 @@ def workload_cases() -> list[QuantCase]:
         QuantCase("wgrad_x_rht16_e1m2_col_e2m3", 8192, 4096, x_wgrad_8192x4096, grid=GRID_E1M2,
                   hadamard_n=16, sign_mask=sign_mask(SIGNS_WGRAD, 16), row_out=False,
                   col_out=True, fmt=FMT_E2M3),
+        # stochastic rounding with 8-bit draws (half the Philox work per element)
+        QuantCase("dy16384_rht16_e1m2_sr8_col", 16384, 4096, dy_16384x4096, grid=GRID_E1M2,
+                  round=SR, hadamard_n=16, sign_mask=sign_mask(SIGNS_DY, 16), row_out=False,
+                  col_out=True, sr_seed=0, sr_bits=8),
+        QuantCase("wgrad_dy_rht16_e1m2_sr8_col_e2m3", 8192, 4096, dy_8192x4096, grid=GRID_E1M2,
+                  round=SR, hadamard_n=16, sign_mask=sign_mask(SIGNS_WGRAD, 16), row_out=False,
+                  col_out=True, fmt=FMT_E2M3, sr_seed=SR_SEED_WGRAD, sr_bits=8),
     ]
