@@ -23,7 +23,7 @@ OUT_F32, OUT_BF16 = 0, 1
 SIGNS_MASK, SIGNS_PER_BLOCK = 0, 1
 
 SYMBOLS = ("mxq_quantize", "mxq_quantize_batch", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "mxq_bias_stats",
-           "mxq_bias_stats_workspace_size", "mxq_round_to_grid", "mxq_rht_sign_mask", "mxq_rotate",
+           "mxq_bias_stats_workspace_size", "mxq_bias_stats_noalloc", "mxq_round_to_grid", "mxq_rht_sign_mask", "mxq_rotate",
            "mxq_status_string", "mxq_abi_version")
 
 
@@ -82,6 +82,8 @@ def lib() -> C.CDLL:
         L.mxq_rht_sign_mask.restype = C.c_uint32
         L.mxq_bias_stats.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, i32, C.POINTER(QTensor),
                                      P, P, C.c_size_t, P]
+        L.mxq_bias_stats_noalloc.argtypes = [C.POINTER(QConfig), P, i64, i64, i64, i32,
+                                             C.POINTER(QTensor), P, P]
         L.mxq_bias_stats_workspace_size.argtypes = [i64, i64, i32]
         L.mxq_bias_stats_workspace_size.restype = C.c_size_t
         L.mxq_round_to_grid.argtypes = [i32, i32, i32, P, P, i64, P, P]
@@ -89,7 +91,7 @@ def lib() -> C.CDLL:
         L.mxq_status_string.restype = C.c_char_p
         L.mxq_abi_version.restype = i32
         for name in ("mxq_quantize", "mxq_quantize_batch", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt",
-                     "mxq_bias_stats", "mxq_round_to_grid", "mxq_rotate"):
+                     "mxq_bias_stats", "mxq_bias_stats_noalloc", "mxq_round_to_grid", "mxq_rotate"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -386,12 +388,35 @@ def bias_stats(x, axis: int, codes, scales, fmt: int, grid=GRID_E2M1, round=RTNE
     _check("mxq_bias_stats", lib().mxq_bias_stats(C.byref(cfg), _ptr(x), rows, cols, x.stride(0),
                                                   axis, C.byref(q), _ptr(out), _ptr(ws), wsb,
                                                   _stream(stream)))
-    raw = bytes(out.cpu().numpy().tobytes())
-    st = Stats.from_buffer_copy(raw)
+    return _stats_dict(out)
+
+
+def _stats_dict(out) -> dict:
+    """The mxq_stats a call wrote into the device byte tensor `out`."""
+    st = Stats.from_buffer_copy(bytes(out.cpu().numpy().tobytes()))
     d = {k: getattr(st, k) for k, _ in Stats._fields_}
     d["level_err_norm"] = list(st.level_err_norm)
     d["level_count"] = list(st.level_count)
     return d
+
+
+def bias_stats_noalloc(x, axis: int, codes, scales, fmt: int, out=None, grid=GRID_E2M1, round=RTNE,
+                       hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0, sr_bits=16, stream=None,
+                       sign_mode=SIGNS_MASK, sign_seed=0, raw=False):
+    """mxq_bias_stats_noalloc into `out` (a device byte tensor of sizeof(mxq_stats),
+    allocated here when not given); returns the stats dict, or `out` itself
+    when raw=True (no host copy)."""
+    import torch
+    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits, sign_mode,
+                  sign_seed)
+    rows, cols = x.shape
+    if out is None:
+        out = torch.zeros(C.sizeof(Stats), dtype=torch.uint8, device=x.device)
+    q = qtensor(codes, scales, fmt, grid)
+    _check("mxq_bias_stats_noalloc",
+           lib().mxq_bias_stats_noalloc(C.byref(cfg), _ptr(x), rows, cols, x.stride(0), axis,
+                                        C.byref(q), _ptr(out), _stream(stream)))
+    return out if raw else _stats_dict(out)
 
 
 # largest magnitude code each grid emits

@@ -22,7 +22,8 @@
  *
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no mutable global state.
+ *    allocates nothing and keeps no mutable global state, except the static
+ *    per-device workspace of mxq_bias_stats_noalloc (below).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    Work is enqueued asynchronously; nothing is synchronized.
  *  - Arguments are validated on the host before any launch; on failure the
@@ -41,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 3
+#define MXQ_ABI_VERSION 4
 
 typedef int32_t mxq_status;
 #define MXQ_OK 0
@@ -283,6 +284,20 @@ mxq_status mxq_bias_stats(const mxq_qconfig *cfg, const void *x, int64_t rows, i
                           int64_t ld_x, int32_t axis, const mxq_qtensor *q, mxq_stats *out,
                           void *workspace, size_t ws_bytes, void *stream);
 size_t mxq_bias_stats_workspace_size(int64_t rows, int64_t cols, int32_t axis);
+
+/* mxq_bias_stats for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without the workspace, the same checks, status codes and
+ * results.  The workspace is a static device array of 204800 bytes that
+ * each GPU holds until the process ends, found on the first call on a device
+ * (with that device current; `stream` must belong to the current device).
+ * A call that would need more returns MXQ_ERR_WORKSPACE (none does: the
+ * workspace is at most 204800 bytes for any size).  The call allocates
+ * nothing.  Every call on one GPU shares its array: calls that overlap on
+ * one GPU race. */
+mxq_status mxq_bias_stats_noalloc(const mxq_qconfig *cfg, const void *x, int64_t rows,
+                                  int64_t cols, int64_t ld_x, int32_t axis, const mxq_qtensor *q,
+                                  mxq_stats *out, void *stream);
 
 /* The rounding step of mxq_quantize on its own, for checks of every input
  * value: codes[i] = the sign-magnitude nibble of a[i] (a value already

@@ -35,7 +35,7 @@ def test_abi_version_and_status_strings(mxq_lib):
     L = mxq_lib.lib()
     import re
     hdr = open(os.path.join(ROOT, "include", "mxq.h")).read()
-    assert L.mxq_abi_version() == int(re.search(r"#define MXQ_ABI_VERSION (\d+)", hdr).group(1)) == 3
+    assert L.mxq_abi_version() == int(re.search(r"#define MXQ_ABI_VERSION (\d+)", hdr).group(1)) == 4
     for s in range(7):
         assert mxq_lib.status_string(s)
     assert mxq_lib.status_string(0) == "ok"
