@@ -1,4 +1,6 @@
 // Version, status strings and host helpers of the libmxq C ABI.
+#include <math.h>
+
 #include "mxq.h"
 
 extern "C" const char *mxq_status_string(mxq_status s)
@@ -44,4 +46,29 @@ extern "C" uint32_t mxq_rht_sign_mask(uint64_t seed, uint32_t n)
     uint32_t ctr[4] = {0u, 0xFFFFFFFFu, 0xFFFFFFFFu, 0xFFFFFFFFu};
     philox_host(ctr, (uint32_t)seed, (uint32_t)(seed >> 32));
     return n == 32 ? ctr[0] : (ctr[0] & 0xFFFFu);
+}
+
+// Effective bucket ratio exp(H) / L of a tensor's magnitude-code histogram
+// (H its entropy in nats, L the number of levels the grid emits).
+extern "C" double mxq_bucket_ratio(const mxq_stats *stats, int32_t grid)
+{
+    const int L = (grid == MXQ_GRID_E2M1 || grid == MXQ_GRID_E1M2) ? 8
+                  : grid == MXQ_GRID_E2M1_MAX4                     ? 7
+                  : grid == MXQ_GRID_E2M1_MAX3                     ? 6
+                                                                   : 0;
+    if (!stats || L == 0)
+        return NAN;
+    double n = 0.0;
+    for (int m = 0; m < L; ++m)
+        n += (double)stats->level_count[m];
+    if (!(n > 0.0))
+        return NAN;
+    double h = 0.0;
+    for (int m = 0; m < L; ++m) {
+        if (stats->level_count[m] == 0)
+            continue;
+        const double p = (double)stats->level_count[m] / n;
+        h -= p * log(p);
+    }
+    return exp(h) / L;
 }

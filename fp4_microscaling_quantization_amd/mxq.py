@@ -23,7 +23,7 @@ OUT_F32, OUT_BF16 = 0, 1
 SIGNS_MASK, SIGNS_PER_BLOCK = 0, 1
 
 SYMBOLS = ("mxq_quantize", "mxq_quantize_batch", "mxq_dequantize", "mxq_wgrad_gemm", "mxq_gemm_abt", "mxq_bias_stats",
-           "mxq_bias_stats_workspace_size", "mxq_bias_stats_noalloc", "mxq_round_to_grid", "mxq_rht_sign_mask", "mxq_rotate",
+           "mxq_bias_stats_workspace_size", "mxq_bias_stats_noalloc", "mxq_bucket_ratio", "mxq_round_to_grid", "mxq_rht_sign_mask", "mxq_rotate",
            "mxq_status_string", "mxq_abi_version")
 
 
@@ -87,6 +87,8 @@ def lib() -> C.CDLL:
         L.mxq_bias_stats_workspace_size.argtypes = [i64, i64, i32]
         L.mxq_bias_stats_workspace_size.restype = C.c_size_t
         L.mxq_round_to_grid.argtypes = [i32, i32, i32, P, P, i64, P, P]
+        L.mxq_bucket_ratio.argtypes = [C.POINTER(Stats), i32]
+        L.mxq_bucket_ratio.restype = C.c_double
         L.mxq_status_string.argtypes = [i32]
         L.mxq_status_string.restype = C.c_char_p
         L.mxq_abi_version.restype = i32
@@ -419,26 +421,12 @@ def bias_stats_noalloc(x, axis: int, codes, scales, fmt: int, out=None, grid=GRI
     return out if raw else _stats_dict(out)
 
 
-# largest magnitude code each grid emits
-GRID_TOP = {GRID_E2M1: 7, GRID_E1M2: 7, GRID_E2M1_MAX4: 6, GRID_E2M1_MAX3: 5}
-
-
 def bucket_ratio(level_count, grid: int) -> float:
-    """Effective bucket ratio of a quantized tensor: exp(H) / L, with H the
-    entropy (nats) of its magnitude-code histogram and L the number of
-    magnitude levels the grid emits (8, or 7 / 6 for E2M1 capped at 4 / 3).
-    1 when every level is used equally, 1/L when all elements share one.
-    The gist.science summary "Repensando o Vies de Encolhimento ... em FP4"
-    ("Resultados Experimentais") reports this ratio rising under the Hadamard
-    rotation without defining it; this is the plainest count-based reading."""
-    import math
-    L = GRID_TOP[grid] + 1
-    counts = [float(c) for c in level_count[:L]]
-    n = sum(counts)
-    if n <= 0:
-        return float("nan")
-    h = -sum(c / n * math.log(c / n) for c in counts if c > 0)
-    return math.exp(h) / L
+    """mxq_bucket_ratio on a histogram of magnitude codes (8 counts)."""
+    st = Stats()
+    for m, c in enumerate(level_count[:8]):
+        st.level_count[m] = int(c)
+    return float(lib().mxq_bucket_ratio(C.byref(st), grid))
 
 
 def round_to_grid(a, grid: int, round=RTNE, rand=None, sr_bits=16, out=None, stream=None):

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 4
+#define MXQ_ABI_VERSION 5
 
 typedef int32_t mxq_status;
 #define MXQ_OK 0
@@ -283,7 +283,19 @@ mxq_status mxq_gemm_abt(const mxq_qtensor *a, const mxq_qtensor *b, int64_t m, i
 mxq_status mxq_bias_stats(const mxq_qconfig *cfg, const void *x, int64_t rows, int64_t cols,
                           int64_t ld_x, int32_t axis, const mxq_qtensor *q, mxq_stats *out,
                           void *workspace, size_t ws_bytes, void *stream);
+/* Utility (no passage defines it): the workspace mxq_bias_stats needs, in
+ * bytes (0 for negative sizes). */
 size_t mxq_bias_stats_workspace_size(int64_t rows, int64_t cols, int32_t axis);
+
+/* The effective bucket ratio that the shrinkage-bias summary ("Resultados
+ * Experimentais") reports rising under the Hadamard rotation, which the
+ * pages do not define; read here as exp(H) / L, with H the entropy (nats) of
+ * the magnitude-code histogram stats->level_count and L the number of levels
+ * `grid` emits (8; 7 and 6 for E2M1 capped at 4 and 3).  1 when all levels are
+ * used equally, 1/L when all elements share one.  Host function: `stats` is a
+ * HOST pointer (an mxq_stats copied back from the device).  Returns NaN for a
+ * NULL pointer, an unknown grid or an empty histogram. */
+double mxq_bucket_ratio(const mxq_stats *stats, int32_t grid);
 
 /* mxq_bias_stats for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
@@ -318,6 +330,8 @@ mxq_status mxq_round_to_grid(int32_t grid, int32_t round, int32_t sr_bits, const
  * stochastic-rounding stream uses.  Host function; returns 0 for other n. */
 uint32_t mxq_rht_sign_mask(uint64_t seed, uint32_t n);
 
+/* Utilities (no passage defines them): a static description of a status
+ * code, and the ABI version the library was built with (MXQ_ABI_VERSION). */
 const char *mxq_status_string(mxq_status s);
 int32_t mxq_abi_version(void);
 

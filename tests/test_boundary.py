@@ -35,7 +35,7 @@ def test_abi_version_and_status_strings(mxq_lib):
     L = mxq_lib.lib()
     import re
     hdr = open(os.path.join(ROOT, "include", "mxq.h")).read()
-    assert L.mxq_abi_version() == int(re.search(r"#define MXQ_ABI_VERSION (\d+)", hdr).group(1)) == 4
+    assert L.mxq_abi_version() == int(re.search(r"#define MXQ_ABI_VERSION (\d+)", hdr).group(1)) == 5
     for s in range(7):
         assert mxq_lib.status_string(s)
     assert mxq_lib.status_string(0) == "ok"
@@ -170,6 +170,42 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower() or f == "synth.py", f
+
+
+def test_binding_is_argument_marshalling_only():
+    """The Python binding computes nothing of the method: it imports no math
+    or array library, holds no floating-point literal, and uses no true
+    division, power or math call; its only arithmetic is integer buffer
+    sizing (block and tile counts).  Every diagnostic it exposes calls the
+    library (the bucket ratio is mxq_bucket_ratio)."""
+    import ast
+    src = open(os.path.join(ROOT, "fp4_microscaling_quantization_amd", "mxq.py")).read()
+    tree = ast.parse(src)
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.Import, ast.ImportFrom)):
+            mods = [a.name for a in node.names] if isinstance(node, ast.Import) else [node.module]
+            for m in mods:
+                assert m.split(".")[0] not in ("math", "numpy", "statistics", "cmath", "scipy"), m
+        if isinstance(node, ast.Constant) and isinstance(node.value, float):
+            raise AssertionError(f"float literal {node.value} at line {node.lineno}")
+        if isinstance(node, ast.BinOp):
+            assert not isinstance(node.op, (ast.Div, ast.Pow)), node.lineno
+        if isinstance(node, ast.Attribute) and isinstance(node.value, ast.Name):
+            assert node.value.id not in ("math", "np", "numpy"), node.lineno
+
+
+def test_bucket_ratio_is_the_library_call(mxq_lib):
+    # the binding's bucket_ratio is marshalling around mxq_bucket_ratio
+    import ctypes as C
+    L = mxq_lib.lib()
+    st = mxq_lib.Stats()
+    for m, c in enumerate([3, 1, 0, 4, 0, 0, 0, 2]):
+        st.level_count[m] = c
+    assert L.mxq_bucket_ratio(C.byref(st), mxq_lib.GRID_E1M2) == \
+        mxq_lib.bucket_ratio([3, 1, 0, 4, 0, 0, 0, 2], mxq_lib.GRID_E1M2)
+    import math
+    assert math.isnan(L.mxq_bucket_ratio(None, 0))
+    assert math.isnan(L.mxq_bucket_ratio(C.byref(st), 9))
 
 
 def test_rht_sign_mask_is_philox_word0(mxq_lib, orc):

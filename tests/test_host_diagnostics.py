@@ -1,5 +1,6 @@
-"""CPU checks of the host-side diagnostics of the Python binding (no GPU):
-the effective bucket ratio exp(H)/L against its closed forms."""
+"""CPU checks of the library's host-side diagnostic mxq_bucket_ratio (no GPU
+needed: it is a host function of libmxq): the effective bucket ratio exp(H)/L
+against its closed forms."""
 import math
 
 import numpy as np
