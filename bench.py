@@ -101,6 +101,16 @@ def launch_percentiles(us: list) -> dict:
             "p90_us": round(q(0.9), 3), "launches": len(xs)}
 
 
+# Rotating input/output sets of every timed loop span more than the 256 MB
+# last-level cache (the MALL), so back-to-back launches cannot be served from it.
+ROTATE_BYTES = 640 << 20
+
+
+def n_sets(set_bytes: float, at_least: int = 4) -> int:
+    """Rotating sets needed for set_bytes each to span ROTATE_BYTES."""
+    return max(at_least, -(-ROTATE_BYTES // max(int(set_bytes), 1)))
+
+
 def quant_bytes_per_elem(fmt: int) -> float:
     # read bf16 (2 B) + write codes (0.5 B FP4 / 0.75 B E2M3) + 1 scale byte per 32
     return 2.0 + (0.5 if fmt == 0 else 0.75) + 1.0 / 32
@@ -183,6 +193,11 @@ def parse():
                     help="launches per kernel for the per-launch duration distribution (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--workloads-only", default=None, metavar="NAMES",
+                    help="time only these workload quantize calls (comma-separated case "
+                         "names, or 'all') and print their JSON object; for counter runs")
+    ap.add_argument("--no-sr8", action="store_true",
+                    help="skip the timing of the batched pair with 8-bit SR draws for dY")
     return ap.parse_args()
 
 
@@ -202,6 +217,14 @@ def main():
     mxq.lib()  # fail loudly if the HIP library is not built
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.workloads_only is not None:
+        only = None if args.workloads_only == "all" else set(args.workloads_only.split(","))
+        if args.copy_calib:
+            copy_calibration(torch, dev)
+        rep = workloads_report(torch, mxq, synth, dev, max(args.steps, 10), only)
+        print(json.dumps({"workloads": rep}), flush=True)
+        return
 
     grid = mxq.GRID_E1M2 if args.variant == "e1m2" else mxq.GRID_E2M1
     fmt = mxq.FMT_E2M3 if args.variant == "e1m2" else mxq.FMT_FP4
@@ -280,6 +303,24 @@ def main():
         return timed(lambda i: calls[i % len(calls)][j](), args.steps) / args.steps
     t_qp, t_gm, t_qdy, t_qx = (own_loop(j) for j in range(4))
 
+    # the same batched pair with 8-bit draws for dY's stochastic rounding
+    # (half the Philox work per element), and dY alone that way
+    if not args.no_sr8:
+        cfg_dy8 = mxq.qconfig(grid=grid, round=mxq.SR, hadamard_n=16, sign_mask=signs,
+                              sr_seed=synth.SR_SEED_WGRAD, sr_bits=8)
+        calls8 = []
+        for dy, xx, qd, qx, c in sets:
+            col_dy = (qd[0], qd[1], fmt, mxq.LAYOUT_MFMA)
+            col_x = (qx[0], qx[1], fmt, mxq.LAYOUT_MFMA)
+            calls8.append((mxq.prepare_quantize_batch([(cfg_x, xx, None, col_x),
+                                                       (cfg_dy8, dy, None, col_dy)]),
+                           mxq.prepare_quantize(cfg_dy8, dy, col=col_dy)))
+
+        def own_loop8(j):
+            time.sleep(0.05)
+            return timed(lambda i: calls8[i % len(calls8)][j](), args.steps) / args.steps
+        t8_pair, t8_dy = own_loop8(0), own_loop8(1)
+
     # per-launch durations: n launches of one kernel back to back over the
     # rotating sets, an event recorded after each (events that take no system
     # fence, so the launches stay back to back); duration i = event i to i + 1
@@ -349,6 +390,9 @@ def main():
             "dy_col_sr_us": round(t_qdy * 1e6, 3), "x_col_rtne_us": round(t_qx * 1e6, 3),
             "both_gbs": round(2 * qbytes / (t_qdy + t_qx) / 1e9, 2),
             "batched_speedup": round((t_qdy + t_qx) / t_qp, 4)},
+        "quantize_sr8": None if args.no_sr8 else {
+            "pair_us": round(t8_pair * 1e6, 3), "pair_gbs": round(2 * qbytes / t8_pair / 1e9, 2),
+            "dy_col_sr8_us": round(t8_dy * 1e6, 3), "dy_gbs": round(qbytes / t8_dy / 1e9, 2)},
         "gemm": {"value": round(g_tflops, 2), "unit": "TFLOP/s", "peak": mfma_peak,
                  "frac": round(g_tflops / mfma_peak, 4)},
         "roofline": dom,
@@ -378,19 +422,25 @@ def main():
                                                 max(args.steps, 10), mfma_peak)
 
     if args.copy_calib:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        rec["copy_calib_bytes"] = 1 << 30
+        rec["copy_calib_bytes"] = copy_calibration(torch, dev)
 
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, args.cpu_seconds)
 
     print(json.dumps(rec), flush=True)
+
+
+def copy_calibration(torch, dev) -> int:
+    """Three plain 1 GiB device-to-device copies: the kernel whose known byte
+    count scales rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return 1 << 30
 
 
 def context_report(torch, dev, kernels):
@@ -566,7 +616,8 @@ def fusion_ratios(torch, mxq, synth, dev, reps):
     then the plain quantizer reading it back), on the activation workload
     (X 8192 x 4096, row-wise, H16) and the weight workload (W 14336 x 4096,
     row- and column-wise outputs, H32 + random signs).  Each variant is timed
-    as `reps` back-to-back launches over two input/output sets."""
+    as `reps` back-to-back launches over rotating input/output sets whose
+    quantizer bytes span more than the last-level cache (n_sets)."""
     import numpy as np
 
     def timed(calls):
@@ -596,8 +647,10 @@ def fusion_ratios(torch, mxq, synth, dev, reps):
     for name, x_np, hn, mask, row, col in workloads:
         rows, cols = x_np.shape
         sets = []
-        for _ in range(2):
-            x = to_dev(x_np)
+        x0 = to_dev(x_np)
+        touched = rows * cols * (2.0 + (int(row) + int(col)) * (0.5 + 1.0 / 32))
+        for i in range(n_sets(touched)):
+            x = x0 if i == 0 else x0.clone()
             r = mxq.empty_qtensor(rows, cols, mxq.FMT_FP4, dev) if row else None
             c = mxq.empty_qtensor(cols, rows, mxq.FMT_FP4, dev) if col else None
             rot_r = torch.empty_like(x) if row else None
@@ -620,7 +673,7 @@ def fusion_ratios(torch, mxq, synth, dev, reps):
                 u.append(mxq.prepare_quantize(c0, rot_c, col=co))
             unfused.append(u)
         tf, tp, tu = timed(fused), timed(plain), timed(unfused)
-        out[name] = {"fused_us": round(tf, 2), "standalone_us": round(tp, 2),
+        out[name] = {"sets": len(sets), "fused_us": round(tf, 2), "standalone_us": round(tp, 2),
                      "unfused_us": round(tu, 2),
                      "fused_over_standalone": round(tf / tp, 3),
                      "unfused_over_fused": round(tu / tf, 3)}
@@ -629,24 +682,32 @@ def fusion_ratios(torch, mxq, synth, dev, reps):
     return out
 
 
-def workloads_report(torch, mxq, synth, dev, reps):
+def workloads_report(torch, mxq, synth, dev, reps, only=None):
     """Every full-size quantize call of the five workloads (the parity tests'
     cases: the 1024 x 1024 activation, the 8192 x 4096 activation with both
     grids, the 14336 x 4096 weight with both outputs and both grids, the
     16384 x 4096 gradient with SR, and the two Wgrad operands) in its own
-    back-to-back loop over two input/output sets: average launch time and
-    algorithmic bandwidth (2 B read per element; per output 0.5 or 0.75 B of
-    codes plus 1/32 B of scale per element)."""
+    back-to-back loop over rotating input/output sets that span more than
+    the last-level cache (n_sets): average launch time and algorithmic
+    bandwidth (2 B read per element; per output 0.5 or 0.75 B of codes plus
+    1/32 B of scale per element).  `only`: the case names to run (all if
+    None)."""
     import numpy as np
     out = {}
     s = torch.cuda.current_stream()
     for case in synth.workload_cases():
+        if only is not None and case.name not in only:
+            continue
         x_np = case.make()
         rows, cols = x_np.shape
         cfg = mxq.qconfig(**case.knobs())
+        nout = int(case.row_out) + int(case.col_out)
+        out_bytes = quant_bytes_per_elem(case.fmt) - 2.0     # codes + scale per element
+        nbytes = rows * cols * (2.0 + nout * out_bytes)
         calls = []
-        for _ in range(2):
-            x = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+        x0 = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
+        for i in range(n_sets(nbytes)):
+            x = x0 if i == 0 else x0.clone()
             r = mxq.empty_qtensor(rows, cols, case.fmt, dev) if case.row_out else None
             c = mxq.empty_qtensor(cols, rows, case.fmt, dev) if case.col_out else None
             calls.append(mxq.prepare_quantize(cfg, x, row=(r[0], r[1], case.fmt) if r else None,
@@ -658,14 +719,12 @@ def workloads_report(torch, mxq, synth, dev, reps):
         e0, e1 = HipEvent(), HipEvent()
         e0.record(s)
         for i in range(reps):
-            calls[i % 2]()
+            calls[i % len(calls)]()
         e1.record(s)
         torch.cuda.synchronize()
         t = e0.elapsed_ms(e1) * 1e-3 / reps
-        nout = int(case.row_out) + int(case.col_out)
-        out_bytes = quant_bytes_per_elem(case.fmt) - 2.0     # codes + scale per element
-        nbytes = rows * cols * (2.0 + nout * out_bytes)
-        out[case.name] = {"avg_us": round(t * 1e6, 2), "GBps": round(nbytes / t / 1e9, 1),
+        out[case.name] = {"sets": len(calls), "avg_us": round(t * 1e6, 2),
+                          "GBps": round(nbytes / t / 1e9, 1),
                           "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
         del calls
         torch.cuda.empty_cache()
@@ -677,7 +736,8 @@ def layer_gemms_report(torch, mxq, synth, dev, grid, fmt, reps, peak):
     N = 14336) through mxq_gemm_abt, with operands in the matrix-core layout
     as the layer GEMM parity tests build them: Fprop Y = X W^T (m = 8192,
     n = 14336, k = 4096) and Dgrad dX = dY W (m = 8192, n = 4096, k = 14336).
-    Each product runs `reps` times back to back over two output buffers."""
+    Each product runs `reps` times back to back over rotating operand and
+    output sets that span more than the last-level cache."""
     import numpy as np
     T_, K_, N_ = 8192, 4096, 14336
     lay = mxq.LAYOUT_MFMA
@@ -697,9 +757,16 @@ def layer_gemms_report(torch, mxq, synth, dev, grid, fmt, reps, peak):
     s = torch.cuda.current_stream()
     for name, a, b, m, n, k in (("fprop", qx, qw["row"], T_, N_, K_),
                                 ("dgrad", qd, qw["col"], T_, K_, N_)):
-        cs = [torch.empty((m, n), dtype=torch.float32, device=dev) for _ in range(2)]
-        calls = [mxq.prepare_wgrad_gemm(a[0], a[1], fmt, grid, b[0], b[1], fmt, grid, c, lay,
-                                        m, n, k, entry="mxq_gemm_abt") for c in cs]
+        # rotating sets: operand copies and outputs spanning the last-level cache
+        set_bytes = sum(t.numel() for t in (a[0], a[1], b[0], b[1])) + 4 * m * n
+        calls, keep = [], []
+        for i in range(n_sets(set_bytes)):
+            ai = a if i == 0 else (a[0].clone(), a[1].clone())
+            bi = b if i == 0 else (b[0].clone(), b[1].clone())
+            c = torch.empty((m, n), dtype=torch.float32, device=dev)
+            keep.append((ai, bi, c))
+            calls.append(mxq.prepare_wgrad_gemm(ai[0], ai[1], fmt, grid, bi[0], bi[1], fmt, grid,
+                                                c, lay, m, n, k, entry="mxq_gemm_abt"))
         for c in calls:
             c()
         torch.cuda.synchronize()
@@ -707,14 +774,14 @@ def layer_gemms_report(torch, mxq, synth, dev, grid, fmt, reps, peak):
         e0, e1 = HipEvent(), HipEvent()
         e0.record(s)
         for i in range(reps):
-            calls[i % 2]()
+            calls[i % len(calls)]()
         e1.record(s)
         torch.cuda.synchronize()
         t = e0.elapsed_ms(e1) * 1e-3 / reps
         tf = 2.0 * m * n * k / t / 1e12
-        out[name] = {"m": m, "n": n, "k": k, "avg_us": round(t * 1e6, 2),
+        out[name] = {"m": m, "n": n, "k": k, "sets": len(calls), "avg_us": round(t * 1e6, 2),
                      "TFLOP_s": round(tf, 1), "frac": round(tf / peak, 4)}
-        del cs, calls
+        del keep, calls
         torch.cuda.empty_cache()
     return out
 

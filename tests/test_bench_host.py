@@ -76,3 +76,11 @@ def test_threaded_oracle_matches_one_call():
     parts = [orc.quantize_lines(x, orc.AXIS_COL, p, a, b - a, 1) for a, b in bench.split_range(96, 5)]
     assert np.array_equal(np.concatenate([c for c, _ in parts]), whole[0])
     assert np.array_equal(np.concatenate([s for _, s in parts]), whole[1])
+
+
+def test_rotating_sets_span_the_last_level_cache():
+    # every timed loop rotates at least 4 sets, together above 512 MB (the
+    # MI355X last-level cache is 256 MB)
+    for set_bytes in (2_654_208, 84_934_656, 179_830_784, 169_869_312, 700 << 20):
+        n = bench.n_sets(set_bytes)
+        assert n >= 4 and n * set_bytes > 512 << 20, (set_bytes, n)
