@@ -617,7 +617,8 @@ def fusion_ratios(torch, mxq, synth, dev, reps):
     (X 8192 x 4096, row-wise, H16) and the weight workload (W 14336 x 4096,
     row- and column-wise outputs, H32 + random signs).  Each variant is timed
     as `reps` back-to-back launches over rotating input/output sets whose
-    quantizer bytes span more than the last-level cache (n_sets)."""
+    quantizer bytes span more than the last-level cache (n_sets), twice in
+    turn with the others; the faster of its two passes is reported."""
     import numpy as np
 
     def timed(calls):
@@ -672,7 +673,19 @@ def fusion_ratios(torch, mxq, synth, dev, reps):
                 u.append(mxq.prepare_rotate(x, mxq.AXIS_COL, hn, mask, mxq.OUT_BF16, rot_c))
                 u.append(mxq.prepare_quantize(c0, rot_c, col=co))
             unfused.append(u)
-        tf, tp, tu = timed(fused), timed(plain), timed(unfused)
+        # two passes over the three pipelines, each after a short idle gap; the
+        # faster pass of each counts (the first loop after setup runs while the
+        # clocks are still ramping)
+        tf = tp = tu = float("inf")
+        for _ in range(2):
+            for which in ("f", "p", "u"):
+                time.sleep(0.05)
+                if which == "f":
+                    tf = min(tf, timed(fused))
+                elif which == "p":
+                    tp = min(tp, timed(plain))
+                else:
+                    tu = min(tu, timed(unfused))
         out[name] = {"sets": len(sets), "fused_us": round(tf, 2), "standalone_us": round(tp, 2),
                      "unfused_us": round(tu, 2),
                      "fused_over_standalone": round(tf / tp, 3),
