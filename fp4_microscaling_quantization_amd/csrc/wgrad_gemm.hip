@@ -17,6 +17,7 @@
 // column l % 16.
 #include "mxq_device.hpp"
 #include "mxq_host.hpp"
+#include <type_traits>
 
 namespace mxq {
 
@@ -340,6 +341,23 @@ __device__ __forceinline__ void dma16(const uint8_t *g, const uint8_t *l)
                  : "memory");
 }
 
+// The same copy with the global address split into a wave-uniform 64-bit base
+// (scalar registers) and a 32-bit per-lane offset, so a step's new base is
+// scalar arithmetic only.
+__device__ __forceinline__ void dma16_so(const uint8_t *base, uint32_t off, const uint8_t *l)
+{
+    const uint32_t la = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint8_t *)l);
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\t"
+                 "s_mov_b32 m0, %3\n\t"
+                 "s_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\t"
+                 "s_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(la))
+                 : "memory");
+}
+
 __device__ __forceinline__ void wait_all_vm()
 {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
@@ -503,6 +521,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_tiled(const uint8_t *_
 // LDS too: with a 4-step group's first step, the 16 A and 16 B tiles' scale
 // words of that group (2 x 4 KiB, one 1 KiB copy per wave) go into one of two
 // group buffers, and each lane reads its 12 words from there.
+// Between the products the loop holds almost no vector (VALU) instructions,
+// which share the issue slots of the matrix cores: the scale byte of a step is
+// picked by the product instruction itself (op_sel), and the copy addresses are
+// a scalar base per step plus a fixed per-lane offset.
 template <int FA, int FB>
 constexpr int ring3_lds_bytes() { return 3 * 16 * 64 * (blk_bytes<FA>() + blk_bytes<FB>()) + 2 * 8192; }
 
@@ -523,13 +545,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
     static_assert(kWaves == 8, "one scale chunk per wave: 4 of A, 4 of B");
     uint8_t *const scl = smem + 3 * STAGE;                 // 2 group buffers of 8 KiB
 
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    // the wave index is uniform across the wave: taken into a scalar register so
+    // the copy addresses are scalar arithmetic
+    const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
     const int wm = wv >> 2, wn = wv & 3, g = lane >> 4, li = lane & 15;
     int tm, tn;
     tile_of(blockIdx.x, (int)((m + kBM - 1) / kBM), (int)((n + kBN - 1) / kBN), tm, tn);
     const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
     const int64_t ntA = (m + 15) / 16, ntB = (n + 15) / 16;
-    const int64_t nsteps = k / 128;
+    const int nsteps = (int)(k / 128);
 
     // operand chunks, as in k_wgrad_tiled
     constexpr int TBA = 64 * blk_bytes<FA>(), TBB = 64 * blk_bytes<FB>();
@@ -553,18 +577,20 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
     const bool sIsA = wv < 4;
     const int64_t stile = sIsA ? min(m0 / 16 + 4 * (wv & 3) + lane / 16, ntA - 1)
                                : min(n0 / 16 + 4 * (wv & 3) + lane / 16, ntB - 1);
-    const uint8_t *const sbase = (sIsA ? as : bs) + stile * 256 + (lane & 15) * 16;
     const int64_t sstride = (sIsA ? ntA : ntB) * 256;    // bytes per group
-
-    auto stage = [&](int64_t s, uint8_t *buf) {
-        const uint8_t *sa_ = ac + s * ntA * TBA, *sb_ = bc + s * ntB * TBB;
+    // copy sources as a wave-uniform base (scalar registers) plus a 32-bit
+    // per-lane offset (the host keeps one step of an operand below 4 GiB)
+    const uint8_t *const sbase0 = sIsA ? as : bs;
+    const uint32_t soffl = (uint32_t)(stile * 256 + (lane & 15) * 16);
+    auto stage = [&](int s, uint8_t *buf) {
+        const uint8_t *sa_ = ac + (int64_t)s * ntA * TBA, *sb_ = bc + (int64_t)s * ntB * TBB;
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int ch = wv * PER + i;
-            dma16((isA[i] ? sa_ : sb_) + goff[i], buf + (isA[i] ? ch * 1024 : SA + (ch - CA) * 1024));
+            dma16_so(isA[i] ? sa_ : sb_, goff[i], buf + (isA[i] ? ch * 1024 : SA + (ch - CA) * 1024));
         }
         if ((s & 3) == 0)
-            dma16(sbase + (s >> 2) * sstride, scl + ((s >> 2) & 1) * 8192 + wv * 1024);
+            dma16_so(sbase0 + (int64_t)(s >> 2) * sstride, soffl, scl + ((s >> 2) & 1) * 8192 + wv * 1024);
     };
 
     v4f acc[8][4];
@@ -579,7 +605,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
         stage(1, smem + STAGE);
     uint32_t ca[8], cb[4];
     int cur = 0, nxt2 = 2;                  // ring slots of steps s and s + 2
-    for (int64_t s = 0; s < nsteps; ++s) {
+    // One step.  Q = s % 4 is the byte of the scale words the matrix cores use,
+    // selected by the instruction's op_sel, so no scale byte is extracted by a
+    // vector instruction between the products (the loop below unrolls the four
+    // steps of a scale group).
+    auto step = [&](int s, auto QC) {
+        constexpr int Q = decltype(QC)::value;
         // this wave's copies for step s landed (those of step s + 1, issued
         // after them, may still be in flight) ...
         if (s + 1 >= nsteps)
@@ -589,7 +620,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
         else
             __builtin_amdgcn_s_waitcnt(0x0F70 | PER);
         barrier_no_fence();                 // ... and everyone's; step s-1's slot is free
-        if ((s & 3) == 0) {
+        if constexpr (Q == 0) {
             const uint32_t *sg = reinterpret_cast<const uint32_t *>(scl + ((s >> 2) & 1) * 8192);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
@@ -601,25 +632,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
         if (s + 2 < nsteps)
             stage(s + 2, smem + nxt2 * STAGE);
         const uint8_t *st = smem + cur * STAGE;
-        const int sh = 8 * (int)(s & 3);
         v8i bf[4];
-        int sb[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j)
             bf[j] = tiled_fragment<FB>(st + SA, 4 * wn + j, lane);
-            sb[j] = (int)((cb[j] >> sh) & 0xFFu);
-        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const v8i af = tiled_fragment<FA>(st, 8 * wm + i, lane);
-            const int sa = (int)((ca[i] >> sh) & 0xFFu);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af, bf[j], acc[i][j], FA, FB, 0, sa, 0, sb[j]);
+                    af, bf[j], acc[i][j], FA, FB, Q, (int)ca[i], Q, (int)cb[j]);
         }
         cur = cur == 2 ? 0 : cur + 1;
         nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
+    };
+    for (int s = 0; s < nsteps; s += 4) {
+        step(s, std::integral_constant<int, 0>{});
+        if (s + 1 < nsteps) step(s + 1, std::integral_constant<int, 1>{});
+        if (s + 2 < nsteps) step(s + 2, std::integral_constant<int, 2>{});
+        if (s + 3 < nsteps) step(s + 3, std::integral_constant<int, 3>{});
     }
 
 #pragma unroll
@@ -665,7 +697,11 @@ hipError_t launch_tiled(int64_t tiles, hipStream_t s, const uint8_t *ac, const u
                         const uint8_t *bc, const uint8_t *bs, int64_t m, int64_t n, int64_t k,
                         float *c, int64_t ldc)
 {
-    if (reinterpret_cast<uintptr_t>(as) % 16 == 0 && reinterpret_cast<uintptr_t>(bs) % 16 == 0) {
+    const bool offsets32 = ((m + 15) / 16) * 64 * blk_bytes<FA>() < (int64_t(1) << 32) &&
+                           ((n + 15) / 16) * 64 * blk_bytes<FB>() < (int64_t(1) << 32) &&
+                           k / 128 <= 0x7FFFFFFF;
+    if (offsets32 && reinterpret_cast<uintptr_t>(as) % 16 == 0 &&
+        reinterpret_cast<uintptr_t>(bs) % 16 == 0) {
         // scale words copied 16 bytes per lane: the 3-stage ring
         constexpr int lds = ring3_lds_bytes<FA, FB>();
         static const hipError_t attr = hipFuncSetAttribute(
