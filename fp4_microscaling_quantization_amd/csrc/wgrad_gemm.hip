@@ -378,10 +378,15 @@ __device__ __forceinline__ v8i tiled_fragment(const uint8_t *__restrict__ lds, i
         const uint4 q = *reinterpret_cast<const uint4 *>(lds + rt * 1024 + lane * 16);
         r[0] = (int)q.x; r[1] = (int)q.y; r[2] = (int)q.z; r[3] = (int)q.w;
     } else {
-        const uint2 *p = reinterpret_cast<const uint2 *>(lds + rt * 1536 + lane * 24);
-        const uint2 a = p[0], b = p[1], c = p[2];
-        r[0] = (int)a.x; r[1] = (int)a.y; r[2] = (int)b.x;
-        r[3] = (int)b.y; r[4] = (int)c.x; r[5] = (int)c.y;
+        // three 8-byte reads off one base with immediate offsets; volatile keeps
+        // the compiler from pairing words of different fragments into one
+        // read (whose halves then need register moves)
+        typedef __attribute__((address_space(3))) const volatile uint64_t lds_u64;
+        lds_u64 *p = (lds_u64 *)(__attribute__((address_space(3))) const uint8_t *)(lds + rt * 1536 + lane * 24);
+        const uint64_t a = p[0], b = p[1], c = p[2];
+        r[0] = (int)(uint32_t)a; r[1] = (int)(uint32_t)(a >> 32);
+        r[2] = (int)(uint32_t)b; r[3] = (int)(uint32_t)(b >> 32);
+        r[4] = (int)(uint32_t)c; r[5] = (int)(uint32_t)(c >> 32);
     }
     return r;
 }
@@ -636,13 +641,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             bf[j] = tiled_fragment<FB>(st + SA, 4 * wn + j, lane);
+        // A fragment i + 1 is read while fragment i's products issue
+        v8i af[2];
+        af[0] = tiled_fragment<FA>(st, 8 * wm, lane);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const v8i af = tiled_fragment<FA>(st, 8 * wm + i, lane);
+            if (i + 1 < 8)
+                af[(i + 1) & 1] = tiled_fragment<FA>(st, 8 * wm + i + 1, lane);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af, bf[j], acc[i][j], FA, FB, Q, (int)ca[i], Q, (int)cb[j]);
+                    af[i & 1], bf[j], acc[i][j], FA, FB, Q, (int)ca[i], Q, (int)cb[j]);
         }
         cur = cur == 2 ? 0 : cur + 1;
         nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
