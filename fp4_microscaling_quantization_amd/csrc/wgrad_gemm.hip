@@ -530,6 +530,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_tiled(const uint8_t *_
 // which share the issue slots of the matrix cores: the scale byte of a step is
 // picked by the product instruction itself (op_sel), and the copy addresses are
 // a scalar base per step plus a fixed per-lane offset.
+// A step reads all twelve of its fragments before it issues its copies, in the
+// order the products use them: LDS answers a wave's reads in order, so the
+// first product waits for two fragments only, and the copies, whose issue can
+// hold a wave while the address unit is busy, come after the reads instead of
+// in front of them (3-4% faster than reading A fragment i + 1 during row i).
 template <int FA, int FB>
 constexpr int ring3_lds_bytes() { return 3 * 16 * 64 * (blk_bytes<FA>() + blk_bytes<FB>()) + 2 * 8192; }
 
@@ -634,24 +639,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
             for (int j = 0; j < 4; ++j)
                 cb[j] = sg[1024 + (4 * wn + j) * 64 + lane];
         }
-        if (s + 2 < nsteps)
-            stage(s + 2, smem + nxt2 * STAGE);
         const uint8_t *st = smem + cur * STAGE;
+        // every fragment of the step read up front, in the order of use, then
+        // the copies of step s + 2
         v8i bf[4];
+        v8i af[8];
+        af[0] = tiled_fragment<FA>(st, 8 * wm, lane);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             bf[j] = tiled_fragment<FB>(st + SA, 4 * wn + j, lane);
-        // A fragment i + 1 is read while fragment i's products issue
-        v8i af[2];
-        af[0] = tiled_fragment<FA>(st, 8 * wm, lane);
+#pragma unroll
+        for (int i = 1; i < 8; ++i)
+            af[i] = tiled_fragment<FA>(st, 8 * wm + i, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 2 < nsteps)
+            stage(s + 2, smem + nxt2 * STAGE);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            if (i + 1 < 8)
-                af[(i + 1) & 1] = tiled_fragment<FA>(st, 8 * wm + i + 1, lane);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i & 1], bf[j], acc[i][j], FA, FB, Q, (int)ca[i], Q, (int)cb[j]);
+                    af[i], bf[j], acc[i][j], FA, FB, Q, (int)ca[i], Q, (int)cb[j]);
         }
         cur = cur == 2 ? 0 : cur + 1;
         nxt2 = nxt2 == 2 ? 0 : nxt2 + 1;
