@@ -293,7 +293,10 @@ __device__ __forceinline__ void col_tile(int64_t bx, int64_t by, const uint16_t 
                                          const OutDesc &out, int vec, const QKnobs &kn,
                                          uint32_t *stage)
 {
-    const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+    // the wave index as a scalar (it is uniform across the wave): the row band
+    // and the LDS offsets derived from it then take no vector registers, which
+    // keeps the stochastic-rounding bodies at 4 waves per SIMD
+    const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
     const int pos = lane & 1, cg = lane >> 1;
     const int64_t rband = by * 128 + wv * 32;  // rows % 32 == 0
     // A full 128 x 128 tile stages its codes in LDS and writes them as long
