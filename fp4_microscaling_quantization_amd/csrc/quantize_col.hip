@@ -94,11 +94,20 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
     const int EMAX = GRID == kE2M1 ? kn.emax : 1;
     // ---- rotation: fp32 butterflies of stride 1, 2, 4, 8 in the lane, 16 across
     rotate16_raw<HN>(v, pos);
-    if constexpr (HN == 32) {
-        const float c = as_f(0x3E3504F3u);  // fl32(1/sqrt(32))
+    // H32's factor c = fl32(1/sqrt(32)).  Where the rounding below starts with
+    // a plain product (RTNE; SR onto E2M1), c goes into the power-of-two
+    // multiplier instead of a product of its own: fl(v (c 2^k)) = fl(v c) 2^k
+    // while c 2^k is a normal number and the result is too (a result below
+    // the normal range rounds to code 0 either way), and the block maximum of
+    // |fl(v c)| is fl(max |v| c), rounding being monotone.  SR onto E1M2 starts
+    // with a fused multiply-add, whose one rounding would then differ from the
+    // rounded fl(v c): there c stays a product of its own.
+    constexpr float c32 = __builtin_bit_cast(float, 0x3E3504F3u);  // fl32(1/sqrt(32))
+    constexpr bool kFoldC = HN == 32 && (ROUND == kRTNE || GRID == kE2M1);
+    if constexpr (HN == 32 && !kFoldC) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-            v[i] = v[i] * c;
+            v[i] = v[i] * c32;
     }
     // ---- block maximum of |y|
     uint32_t am;
@@ -127,6 +136,8 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
     am = max(am, lane_xor<1>(am));
     if constexpr (HN == 16)
         am = as_u(as_f(am) * 0.25f);  // fl(max|v| / 4) = max |fl(v / 4)|
+    if constexpr (kFoldC)
+        am = as_u(as_f(am) * c32);    // fl(max|v| c) = max |fl(v c)|
     const uint32_t sc = am >= 0x7F800000u ? 0xFFu : (uint32_t)max((int)(am >> 23) - EMAX, 0);
 
     // ---- multiplier m2 = 2 * 2^-e (times 1/4 for H16): v * m2 = 2 y 2^-e
@@ -138,6 +149,8 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
         for (int i = 0; i < 16; ++i) {
             if constexpr (HN == 16)
                 v[i] = v[i] * 0.25f;
+            if constexpr (kFoldC)
+                v[i] = v[i] * c32;
             v[i] = v[i] * inv;
         }
         m2 = 2.0f;
@@ -145,6 +158,17 @@ __device__ __forceinline__ uint32_t col16(float (&v)[16], int pos, uint64_t blk,
         m2 = as_f((255u - min(sc, 253u)) << 23);
         if constexpr (HN == 16)
             m2 *= 0.25f;
+        if constexpr (kFoldC) {
+            if (sc <= 251u) {
+                m2 *= c32;  // c 2^(128 - sc) >= 2^-126: exact
+            } else {
+                // the top codes (and non-finite blocks): c 2^(128 - sc) would be
+                // subnormal, so v takes c first
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[i] = v[i] * c32;
+            }
+        }
     }
 
     // ---- rounding
