@@ -39,6 +39,19 @@ struct QKnobs {
     uint32_t skey_lo, skey_hi;   // key of the per-block signs
 };
 
+// Global-memory views of generic pointers.  A pointer that reaches a kernel
+// inside a structure picked at run time (a job of a batch, an output
+// descriptor) is generic to the compiler, which then accesses it with flat
+// instructions.  Those also count against the LDS and scalar-memory counter,
+// so a wait for an LDS access waits for every load still in flight as well.
+// Every tensor the kernels read or write lives in device global memory.
+#define MXQ_GLOBAL __attribute__((address_space(1)))
+template <class T> __device__ __forceinline__ MXQ_GLOBAL T *gmem(T *p) { return (MXQ_GLOBAL T *)p; }
+// plain vector types for the wide accesses through such views (HIP's uint2 and
+// uint4 have constructors that take generic references only)
+typedef uint32_t gv2u __attribute__((ext_vector_type(2)));
+typedef uint32_t gv4u __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float as_f(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t as_u(float f) { return __float_as_uint(f); }
 

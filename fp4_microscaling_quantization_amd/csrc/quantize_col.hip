@@ -262,8 +262,8 @@ template <int N>
 __device__ __forceinline__ void store_words(const OutDesc &o, uint64_t line, uint64_t jb, int pos,
                                             const uint32_t *w)
 {
-    uint32_t *d = reinterpret_cast<uint32_t *>(o.codes + code_offset(o, line, jb, 8 * N) +
-                                               4 * N * pos);
+    MXQ_GLOBAL uint32_t *d = reinterpret_cast<MXQ_GLOBAL uint32_t *>(
+        gmem(o.codes) + code_offset(o, line, jb, 8 * N) + 4 * N * pos);
 #pragma unroll
     for (int k = 0; k < N; ++k)
         d[k] = w[k];
@@ -291,8 +291,9 @@ __device__ __forceinline__ void flush_stage(const OutDesc &o, const uint32_t *st
 {
     if (o.layout == MXQ_LAYOUT_MFMA) {
         // one run of 128 * BB bytes, 16-byte aligned
-        uint4 *dst = reinterpret_cast<uint4 *>(o.codes + code_offset(o, line0, jb0, BB));
-        const uint4 *src = reinterpret_cast<const uint4 *>(stage);
+        MXQ_GLOBAL gv4u *dst =
+            reinterpret_cast<MXQ_GLOBAL gv4u *>(gmem(o.codes) + code_offset(o, line0, jb0, BB));
+        const gv4u *src = reinterpret_cast<const gv4u *>(stage);
 #pragma unroll
         for (int k = 0; k < BB / 8; ++k)
             dst[k * 256 + t] = src[k * 256 + t];
@@ -302,7 +303,8 @@ __device__ __forceinline__ void flush_stage(const OutDesc &o, const uint32_t *st
 #pragma unroll
         for (int k = 0; k < W / 2; ++k) {
             const int idx = k * 256 + t, cl = idx / W, q = idx % W;
-            reinterpret_cast<uint32_t *>(o.codes + code_offset(o, line0 + cl, jb0, BB))[q] =
+            reinterpret_cast<MXQ_GLOBAL uint32_t *>(gmem(o.codes) +
+                                                    code_offset(o, line0 + cl, jb0, BB))[q] =
                 stage[cl * W + q];
         }
     }
@@ -339,7 +341,7 @@ __device__ __forceinline__ void col_tile(int64_t bx, int64_t by, const uint16_t 
     if (vec && c0 + 4 <= cols) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const uint2 w = *reinterpret_cast<const uint2 *>(x + (r0 + i) * ld + c0);
+            const gv2u w = *reinterpret_cast<const MXQ_GLOBAL gv2u *>(gmem(x) + (r0 + i) * ld + c0);
             lo[i] = w.x;
             hi[i] = w.y;
         }
@@ -349,7 +351,7 @@ __device__ __forceinline__ void col_tile(int64_t bx, int64_t by, const uint16_t 
             uint32_t hh[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                hh[j] = (c0 + j < cols) ? (uint32_t)x[(r0 + i) * ld + c0 + j] : 0u;
+                hh[j] = (c0 + j < cols) ? (uint32_t)gmem(x)[(r0 + i) * ld + c0 + j] : 0u;
             lo[i] = hh[0] | (hh[1] << 16);
             hi[i] = hh[2] | (hh[3] << 16);
         }
@@ -423,9 +425,9 @@ __device__ __forceinline__ void col_tile(int64_t bx, int64_t by, const uint16_t 
         }
         if (pos == 0) {
             if (ca < cols)
-                out.scales[scale_offset(out, (uint64_t)ca, jb)] = (uint8_t)sa;
+                gmem(out.scales)[scale_offset(out, (uint64_t)ca, jb)] = (uint8_t)sa;
             if (cb < cols)
-                out.scales[scale_offset(out, (uint64_t)cb, jb)] = (uint8_t)sb;
+                gmem(out.scales)[scale_offset(out, (uint64_t)cb, jb)] = (uint8_t)sb;
         }
     }
     if (staged) {
@@ -529,14 +531,14 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
         uint32_t w[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         if (ok) {
             if (vec) {
-                const uint4 q0 = *reinterpret_cast<const uint4 *>(x + off);
-                const uint4 q1 = *reinterpret_cast<const uint4 *>(x + off + 8);
+                const gv4u q0 = *reinterpret_cast<const MXQ_GLOBAL gv4u *>(gmem(x) + off);
+                const gv4u q1 = *reinterpret_cast<const MXQ_GLOBAL gv4u *>(gmem(x) + off + 8);
                 w[0] = q0.x; w[1] = q0.y; w[2] = q0.z; w[3] = q0.w;
                 w[4] = q1.x; w[5] = q1.y; w[6] = q1.z; w[7] = q1.w;
             } else {
 #pragma unroll
                 for (int k = 0; k < 8; ++k)
-                    w[k] = (uint32_t)x[off + 2 * k] | ((uint32_t)x[off + 2 * k + 1] << 16);
+                    w[k] = (uint32_t)gmem(x)[off + 2 * k] | ((uint32_t)gmem(x)[off + 2 * k + 1] << 16);
             }
         }
         const uint32_t sg = block_signs<HN>(kn, jbk[u]) >> (16 * pos);
@@ -586,7 +588,7 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
 #pragma unroll
             for (int d = 0; d < 2; ++d)
                 if (base + 32 * (up + d) + pr < nblocks)
-                    out.scales[scale_offset(out, line[up + d], jbk[up + d])] = (uint8_t)sc[d];
+                    gmem(out.scales)[scale_offset(out, line[up + d], jbk[up + d])] = (uint8_t)sc[d];
         }
     }
 }
@@ -629,7 +631,7 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
         if (vec && c0 + 4 <= cols) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const uint2 w = *reinterpret_cast<const uint2 *>(x + (r0 + i) * ld + c0);
+                const gv2u w = *reinterpret_cast<const MXQ_GLOBAL gv2u *>(gmem(x) + (r0 + i) * ld + c0);
                 lo[i] = w.x;
                 hi[i] = w.y;
             }
@@ -639,7 +641,7 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
                 uint32_t hh[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    hh[j] = (c0 + j < cols) ? (uint32_t)x[(r0 + i) * ld + c0 + j] : 0u;
+                    hh[j] = (c0 + j < cols) ? (uint32_t)gmem(x)[(r0 + i) * ld + c0 + j] : 0u;
                 lo[i] = hh[0] | (hh[1] << 16);
                 hi[i] = hh[2] | (hh[3] << 16);
             }
@@ -707,9 +709,9 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
             }
             if (pos == 0) {
                 if (ca < cols)
-                    cout.scales[scale_offset(cout, (uint64_t)ca, jb)] = (uint8_t)sa;
+                    gmem(cout.scales)[scale_offset(cout, (uint64_t)ca, jb)] = (uint8_t)sa;
                 if (cb < cols)
-                    cout.scales[scale_offset(cout, (uint64_t)cb, jb)] = (uint8_t)sb;
+                    gmem(cout.scales)[scale_offset(cout, (uint64_t)cb, jb)] = (uint8_t)sb;
             }
         }
     }
@@ -786,7 +788,7 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
 #pragma unroll
             for (int d = 0; d < 2; ++d)
                 if (ok[up + d])
-                    rout.scales[scale_offset(rout, rline[up + d], rjb[up + d])] = (uint8_t)sc[d];
+                    gmem(rout.scales)[scale_offset(rout, rline[up + d], rjb[up + d])] = (uint8_t)sc[d];
         }
     }
 }
