@@ -535,6 +535,35 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_tiled(const uint8_t *_
 // first product waits for two fragments only, and the copies, whose issue can
 // hold a wave while the address unit is busy, come after the reads instead of
 // in front of them (3-4% faster than reading A fragment i + 1 during row i).
+// A wave's 128 x 64 accumulator tile to C through 4 KiB of LDS, 16 rows at a
+// time.  Lane (g, li) holds rows 4 g .. 4 g + 3 of column 16 j + li; the rows
+// go back out as 16-byte pieces (lane L: row 4 k + L / 16, columns
+// 4 (L % 16) .. + 3), so each store writes four 256-byte row runs instead of
+// sixteen 64-byte ones.  Element (R, C) of the 16 x 64 slab sits at
+// R * 64 + 4 ((C / 4) ^ (4 (R / 4))) + C % 4, which puts the four row quads of
+// a write on distinct banks.  The stores are nontemporal: C is not read again
+// here, and the operand panels that other workgroups still read keep the cache.
+__device__ __forceinline__ void store_tile_lds(const v4f (&acc)[8][4], float *lw, float *c,
+                                               int64_t ldc, int64_t row0, int64_t col0, int lane)
+{
+    const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                lw[(4 * g + r) * 64 + 4 * ((4 * j + (li >> 2)) ^ (4 * g)) + (li & 3)] = acc[i][j][r];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int R = 4 * k + g;
+            const v4f v = *reinterpret_cast<const v4f *>(lw + R * 64 + 4 * (li ^ (4 * k)));
+            __builtin_nontemporal_store(
+                v, reinterpret_cast<v4f *>(c + (row0 + 16 * i + R) * ldc + col0 + 4 * li));
+        }
+    }
+}
+
 template <int FA, int FB>
 constexpr int ring3_lds_bytes() { return 3 * 16 * 64 * (blk_bytes<FA>() + blk_bytes<FB>()) + 2 * 8192; }
 
@@ -553,6 +582,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
     constexpr int PER = (CA + CB) / kWaves;                // chunks per wave per step
     static_assert(PER * kWaves == CA + CB, "chunks split evenly over the waves");
     static_assert(kWaves == 8, "one scale chunk per wave: 4 of A, 4 of B");
+    static_assert(STAGE >= kWaves * 4096, "a ring slot holds every wave's 4 KiB output slab");
     uint8_t *const scl = smem + 3 * STAGE;                 // 2 group buffers of 8 KiB
 
     // the wave index is uniform across the wave: taken into a scalar register so
@@ -672,6 +702,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
         if (s + 3 < nsteps) step(s + 3, std::integral_constant<int, 3>{});
     }
 
+    // a whole tile leaves through LDS as 16-byte row pieces: the ring slot of
+    // step nsteps (that of step nsteps - 3, read by every wave before the last
+    // barrier, with no copy pending) holds each wave's 4 KiB
+    if (m0 + kBM <= m && n0 + kBN <= n && (ldc & 3) == 0 && ((uintptr_t)c & 15) == 0) {
+        float *lw = reinterpret_cast<float *>(smem + cur * STAGE) + wv * 1024;
+        store_tile_lds(acc, lw, c, ldc, m0 + 128 * wm, n0 + 64 * wn, lane);
+        return;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
