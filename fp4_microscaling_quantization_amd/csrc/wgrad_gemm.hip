@@ -724,6 +724,197 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ring3(const uint8_t *_
         }
 }
 
+// The ring kernel for FP4 operands with the fragment reads one step ahead.
+// In k_wgrad_ring3 every wave reads a step's fragments right after the step's
+// barrier and then issues its products, so all waves read the LDS at the same
+// time and then all keep the matrix cores busy at the same time: the reads
+// and copies add to the products instead of overlapping them.  Here a wave
+// reads step s + 1's fragments into a second register set right after the
+// barrier of step s and then issues step s's products (whose fragments it
+// read during step s - 1), so the LDS reads and the copies run while the
+// products do.  Two fragment sets take 2 x 48 registers with FP4 operands
+// (FP6 would need 2 x 72 and no longer fit two waves per SIMD), and the reads
+// of step s + 1 need its copies landed by the barrier of step s, so the ring
+// has four slots (copies of step s + 3 issued in step s: a two-step lead
+// again).  The loop has no branches (a branch would make the compiler's
+// counter bookkeeping assume the products wait for the reads just issued):
+// k is a multiple of 512, and past the last step the reads are unused and
+// the copies rewrite step s - 1's bytes into its own slot.
+template <int FA, int FB>
+constexpr int ra4_lds_bytes() { return 4 * 16 * 64 * (blk_bytes<FA>() + blk_bytes<FB>()) + 2 * 8192; }
+
+template <int FA, int FB>
+__global__ __launch_bounds__(64 * kWaves, 1) void k_wgrad_ra4(const uint8_t *__restrict__ ac,
+                                                                const uint8_t *__restrict__ as,
+                                                                const uint8_t *__restrict__ bc,
+                                                                const uint8_t *__restrict__ bs,
+                                                                int64_t m, int64_t n, int64_t k,
+                                                                float *__restrict__ c, int64_t ldc)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int SA = 16 * 64 * blk_bytes<FA>(), SB = 16 * 64 * blk_bytes<FB>();
+    constexpr int STAGE = SA + SB;
+    constexpr int CA = SA / 1024, CB = SB / 1024;          // 1 KB chunks per operand
+    constexpr int PER = (CA + CB) / kWaves;                // chunks per wave per step
+    static_assert(PER * kWaves == CA + CB, "chunks split evenly over the waves");
+    static_assert(kWaves == 8, "one scale chunk per wave: 4 of A, 4 of B");
+    static_assert(STAGE >= kWaves * 4096, "a ring slot holds every wave's 4 KiB output slab");
+    uint8_t *const scl = smem + 4 * STAGE;                 // 2 group buffers of 8 KiB
+
+    // the wave index is uniform across the wave: taken into a scalar register so
+    // the copy addresses are scalar arithmetic
+    const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wv >> 2, wn = wv & 3, g = lane >> 4, li = lane & 15;
+    int tm, tn;
+    tile_of(blockIdx.x, (int)((m + kBM - 1) / kBM), (int)((n + kBN - 1) / kBN), tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    const int64_t ntA = (m + 15) / 16, ntB = (n + 15) / 16;
+    const int nsteps = (int)(k / 128);
+
+    // operand chunks: with FP4 a 1 KiB chunk is one 16-row tile, so a chunk's
+    // source is a wave-uniform tile offset plus 16 bytes per lane
+    static_assert(FA == kMfmaFP4 && FB == kMfmaFP4, "FP4 operands only");
+    uint32_t gsc[PER];
+    bool isA[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int ch = wv * PER + i;
+        isA[i] = ch < CA;
+        const int cc = isA[i] ? ch : ch - CA;
+        const int64_t tile = isA[i] ? min(m0 / 16 + cc, ntA - 1) : min(n0 / 16 + cc, ntB - 1);
+        gsc[i] = (uint32_t)(tile * 1024);
+    }
+    const uint32_t lofs = (uint32_t)lane * 16;
+    // this wave's scale chunk of a group: wave w < 4 copies A tiles 4w .. 4w + 3
+    // of the workgroup's 16, wave w >= 4 B tiles 4 (w - 4) ..; lane L carries
+    // the words of lanes 4 (L % 16) .. + 3 of tile 4 (w % 4) + L / 16, so the
+    // buffer holds [A 16 tiles | B 16 tiles][64 lanes][4 B] (tiles past the
+    // operand's last are clamped, as for the codes)
+    const bool sIsA = wv < 4;
+    const int64_t stile = sIsA ? min(m0 / 16 + 4 * (wv & 3) + lane / 16, ntA - 1)
+                               : min(n0 / 16 + 4 * (wv & 3) + lane / 16, ntB - 1);
+    const int64_t sstride = (sIsA ? ntA : ntB) * 256;    // bytes per group
+    // copy sources as a wave-uniform base (scalar registers) plus a 32-bit
+    // per-lane offset (the host keeps one step of an operand below 4 GiB)
+    const uint8_t *const sbase0 = sIsA ? as : bs;
+    const uint32_t soffl = (uint32_t)(stile * 256 + (lane & 15) * 16);
+    auto stage = [&](int s, uint8_t *buf) {
+        const uint8_t *sa_ = ac + (int64_t)s * ntA * 1024, *sb_ = bc + (int64_t)s * ntB * 1024;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ch = wv * PER + i;
+            dma16_so((isA[i] ? sa_ : sb_) + gsc[i], lofs, buf + (isA[i] ? ch * 1024 : SA + (ch - CA) * 1024));
+        }
+        if ((s & 3) == 0)
+            dma16_so(sbase0 + (int64_t)(s >> 2) * sstride, soffl, scl + ((s >> 2) & 1) * 8192 + wv * 1024);
+    };
+
+    v4f acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+    // k % 512 == 0 and k >= 512 (the host checks): nsteps is a multiple of 4
+    stage(0, smem);
+    stage(1, smem + STAGE);
+    stage(2, smem + 2 * STAGE);
+    __builtin_amdgcn_s_waitcnt(0x0070 | (2 * PER));  // step 0's copies landed
+    barrier_no_fence();
+    uint32_t ca[8], cb[4];
+    auto read_scales = [&](int grp) {
+        const uint32_t *sg = reinterpret_cast<const uint32_t *>(scl + (grp & 1) * 8192);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            ca[i] = sg[(8 * wm + i) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            cb[j] = sg[1024 + (4 * wn + j) * 64 + lane];
+    };
+    v8i af[2][8], bf[2][4];
+    auto read_frags = [&](int set, const uint8_t *st) {
+        af[set][0] = tiled_fragment<FA>(st, 8 * wm, lane);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[set][j] = tiled_fragment<FB>(st + SA, 4 * wn + j, lane);
+#pragma unroll
+        for (int i = 1; i < 8; ++i)
+            af[set][i] = tiled_fragment<FA>(st, 8 * wm + i, lane);
+    };
+    read_scales(0);
+    read_frags(0, smem);
+    // One step, without branches.  Its fragments were read during the previous
+    // step; after the barrier the wave reads those of step s + 1 into the other
+    // register set and issues the copies of step s + 3, then the products of
+    // step s run while those reads and copies are in flight.  Past the last
+    // step the reads are left unused and the copies rewrite step s - 1 into
+    // its own slot (the same bytes, and the same number of copies, so the
+    // waits stay exact).
+    auto step = [&](int s, auto QC) {
+        constexpr int Q = decltype(QC)::value;
+        constexpr int P = Q & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        // this wave's copies of step s + 1 landed (those of s + 2 may not
+        // have), and its reads of step s's fragments, issued a step ago
+        if constexpr (((Q + 2) & 3) == 0)
+            __builtin_amdgcn_s_waitcnt(0x0070 | (PER + 1));
+        else
+            __builtin_amdgcn_s_waitcnt(0x0070 | PER);
+        // ... and everyone's; every wave is past the products of step s - 1,
+        // so slot (s - 1) % 4 is free
+        barrier_no_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(P ^ 1, smem + ((Q + 1) & 3) * STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+        stage(s + 3 < nsteps ? s + 3 : s - 1, smem + ((Q + 3) & 3) * STAGE);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af[P][i], bf[P][j], acc[i][j], FA, FB, Q, (int)ca[i], Q, (int)cb[j]);
+        }
+        if constexpr (Q == 3) {
+            // the next group's scale words (copied with step s + 1, which landed)
+            __builtin_amdgcn_sched_barrier(0);
+            read_scales((s + 1) >> 2);
+        }
+    };
+    for (int s = 0; s < nsteps; s += 4) {
+        step(s, std::integral_constant<int, 0>{});
+        step(s + 1, std::integral_constant<int, 1>{});
+        step(s + 2, std::integral_constant<int, 2>{});
+        step(s + 3, std::integral_constant<int, 3>{});
+    }
+    // every wave's copies and reads are done before a slot takes the output
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    barrier_no_fence();
+    const int cur = 0;
+
+    // a whole tile leaves through LDS as 16-byte row pieces: the ring slot of
+    // step nsteps (that of step nsteps - 3, read by every wave before the last
+    // barrier, with no copy pending) holds each wave's 4 KiB
+    if (m0 + kBM <= m && n0 + kBN <= n && (ldc & 3) == 0 && ((uintptr_t)c & 15) == 0) {
+        float *lw = reinterpret_cast<float *>(smem + cur * STAGE) + wv * 1024;
+        store_tile_lds(acc, lw, c, ldc, m0 + 128 * wm, n0 + 64 * wn, lane);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t col = n0 + 64 * wn + 16 * j + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + 128 * wm + 16 * i + 4 * g + r;
+                if (row < m && col < n)
+                    c[row * ldc + col] = acc[i][j][r];
+            }
+        }
+}
+
 __global__ __launch_bounds__(256) void k_zero_fill(float *__restrict__ c, int64_t m, int64_t n,
                                                    int64_t ldc)
 {
@@ -759,6 +950,19 @@ hipError_t launch_tiled(int64_t tiles, hipStream_t s, const uint8_t *ac, const u
     if (offsets32 && reinterpret_cast<uintptr_t>(as) % 16 == 0 &&
         reinterpret_cast<uintptr_t>(bs) % 16 == 0) {
         // scale words copied 16 bytes per lane: the 3-stage ring
+        if constexpr (FA == kMfmaFP4 && FB == kMfmaFP4) {
+            if (k % 512 == 0) {
+                constexpr int lds = ra4_lds_bytes<FA, FB>();
+                static const hipError_t attr = hipFuncSetAttribute(
+                    reinterpret_cast<const void *>(&k_wgrad_ra4<FA, FB>),
+                    hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+                if (attr != hipSuccess)
+                    return attr;
+                hipLaunchKernelGGL((k_wgrad_ra4<FA, FB>), dim3((unsigned)tiles), dim3(64 * kWaves),
+                                   lds, s, ac, as, bc, bs, m, n, k, c, ldc);
+                return hipGetLastError();
+            }
+        }
         constexpr int lds = ring3_lds_bytes<FA, FB>();
         static const hipError_t attr = hipFuncSetAttribute(
             reinterpret_cast<const void *>(&k_wgrad_ring3<FA, FB>),

@@ -241,7 +241,7 @@ def _tiled(orc, codes, scales, fmt):
 
 
 @pytest.mark.parametrize("shape", [(256, 256, 512), (100, 72, 384), (300, 520, 1152), (16, 16, 128),
-                                   (48, 40, 256), (64, 300, 640)])
+                                   (48, 40, 256), (64, 300, 640), (130, 260, 1024), (512, 256, 2048)])
 @pytest.mark.parametrize("combo", COMBOS, ids=lambda c: f"A{c[0]}B{c[1]}")
 def test_gemm_mfma_layout_exact_at_unit_scale(orc, shape, combo):
     from fp4_microscaling_quantization_amd import mxq
