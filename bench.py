@@ -196,6 +196,8 @@ def parse():
     ap.add_argument("--workloads-only", default=None, metavar="NAMES",
                     help="time only these workload quantize calls (comma-separated case "
                          "names, or 'all') and print their JSON object; for counter runs")
+    ap.add_argument("--no-other-form", action="store_true",
+                    help="skip the GEMM timed with the other operand form")
     ap.add_argument("--no-sr8", action="store_true",
                     help="skip the timing of the batched pair with 8-bit SR draws for dY")
     return ap.parse_args()
@@ -405,6 +407,10 @@ def main():
                                "note": "event-to-event interval per launch, an event recorded "
                                        "after each; includes the event's own time"}
 
+    if not args.no_other_form:
+        rec["gemm_other_form"] = other_form_gemm_report(torch, mxq, synth, dev, dy0, x0,
+                                                        args.variant, args.steps)
+
     if not args.no_quality:
         rec["quality"] = quality_report(torch, mxq, synth, dev)
 
@@ -428,6 +434,51 @@ def main():
         rec["cpu_baseline"] = cpu_baseline(dy_np, x_np, cfg_dy, cfg_x, fmt, grid, args.cpu_seconds)
 
     print(json.dumps(rec), flush=True)
+
+
+def other_form_gemm_report(torch, mxq, synth, dev, dy, x, variant, reps):
+    """The step's GEMM with the other operand form, quantized from the same dY
+    and X: FP4 codes on the E2M1 grid when the step runs E1M2 (FP6 operands),
+    and FP6 codes on the E1M2 grid the other way round.  Timed as the step's
+    own GEMM loop: `reps` launches back to back over rotating operand and
+    output sets that span more than the last-level cache."""
+    other = "e2m1" if variant == "e1m2" else "e1m2"
+    grid = mxq.GRID_E2M1 if other == "e2m1" else mxq.GRID_E1M2
+    fmt = mxq.FMT_FP4 if other == "e2m1" else mxq.FMT_E2M3
+    signs = synth.sign_mask(synth.SIGNS_WGRAD, 16)
+    cfg_dy = mxq.qconfig(grid=grid, round=mxq.SR, hadamard_n=16, sign_mask=signs,
+                         sr_seed=synth.SR_SEED_WGRAD)
+    cfg_x = mxq.qconfig(grid=grid, round=mxq.RTNE, hadamard_n=16, sign_mask=signs)
+    qbytes = sum(mxq.qtensor_sizes(L, T, fmt, mxq.LAYOUT_MFMA)[0] for L in (N, K))
+    calls, keep = [], []
+    for i in range(n_sets(qbytes + 4 * N * K)):
+        qd = mxq.empty_qtensor(N, T, fmt, dev, mxq.LAYOUT_MFMA)
+        qx = mxq.empty_qtensor(K, T, fmt, dev, mxq.LAYOUT_MFMA)
+        c = torch.empty((N, K), dtype=torch.float32, device=dev)
+        mxq.quantize_batch([(cfg_x, x, None, (qx[0], qx[1], fmt, mxq.LAYOUT_MFMA)),
+                            (cfg_dy, dy, None, (qd[0], qd[1], fmt, mxq.LAYOUT_MFMA))])
+        keep.append((qd, qx, c))
+        calls.append(mxq.prepare_wgrad_gemm(qd[0], qd[1], fmt, grid, qx[0], qx[1], fmt, grid, c,
+                                            mxq.LAYOUT_MFMA, N, K, T))
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    time.sleep(0.05)
+    s = torch.cuda.current_stream()
+    e0, e1 = HipEvent(), HipEvent()
+    e0.record(s)
+    for i in range(reps):
+        calls[i % len(calls)]()
+    e1.record(s)
+    torch.cuda.synchronize()
+    t = e0.elapsed_ms(e1) * 1e-3 / reps
+    tf = 2.0 * N * K * T / t / 1e12
+    peak = MFMA_PEAK_TFLOPS["fp4" if fmt == mxq.FMT_FP4 else "fp6"]
+    del keep, calls
+    torch.cuda.empty_cache()
+    return {"variant": other, "operands": "FP4" if fmt == mxq.FMT_FP4 else "FP6 E2M3",
+            "sets": n_sets(qbytes + 4 * N * K), "avg_us": round(t * 1e6, 2),
+            "TFLOP_s": round(tf, 1), "frac": round(tf / peak, 4)}
 
 
 def copy_calibration(torch, dev) -> int:
