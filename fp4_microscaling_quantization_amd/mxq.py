@@ -186,7 +186,9 @@ def prepare_quantize(cfg: QConfig, x, row=None, col=None, stream=None):
     """The call quantize_into(cfg, x, row, col) marshalled once: returns a
     function of no arguments that launches it again on the same buffers (for
     timing loops, where per-call argument conversion would leave the GPU
-    waiting on the host)."""
+    waiting on the host).  The function holds every tensor it was given, so
+    their memory cannot be freed and handed to another tensor while it can
+    still launch."""
     rows, cols, ld = x.shape[0], x.shape[1], x.stride(0)
 
     def desc(o):
@@ -199,7 +201,7 @@ def prepare_quantize(cfg: QConfig, x, row=None, col=None, stream=None):
     args = (C.byref(cfg_), _ptr(x), rows, cols, ld, C.byref(rt) if rt else None,
             C.byref(ct) if ct else None, _stream(stream))
     fn = lib().mxq_quantize
-    keep = (cfg_, rt, ct)
+    keep = (cfg_, rt, ct, x, row, col)
 
     def call():
         _check("mxq_quantize", fn(*args))
@@ -230,7 +232,7 @@ def _batch_args(jobs):
             lay = o[3] if len(o) > 3 else LAYOUT_ROWS
             return QTensor(o[0].data_ptr(), o[1].data_ptr(), o[2], cfg_.grid, lay)
         rt, ct = desc(row), desc(col)
-        keep += [cfg_, rt, ct]
+        keep += [cfg_, rt, ct, x, row, col]
         arr[i] = QuantizeJob(C.pointer(cfg_), _addr(x), x.shape[0], x.shape[1], x.stride(0),
                              C.pointer(rt) if rt else None, C.pointer(ct) if ct else None)
     return arr, keep
@@ -246,7 +248,8 @@ def quantize_batch(jobs, stream=None):
 
 
 def prepare_quantize_batch(jobs, stream=None):
-    """quantize_batch(jobs) marshalled once (see prepare_quantize)."""
+    """quantize_batch(jobs) marshalled once (see prepare_quantize; the function
+    holds every job's tensors)."""
     arr, keep = _batch_args(jobs)
     args = (arr, len(jobs), _stream(stream))
     fn = lib().mxq_quantize_batch
@@ -314,7 +317,8 @@ def wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_gri
 def prepare_wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fmt, b_grid, out,
                        layout, m, n, k, stream=None, entry="mxq_wgrad_gemm"):
     """wgrad_gemm(...) marshalled once into a function of no arguments
-    (entry="mxq_gemm_abt" for the same product under its general name)."""
+    (entry="mxq_gemm_abt" for the same product under its general name) that
+    holds every tensor it was given."""
     qa = qtensor(a_codes, a_scales, a_fmt, a_grid, layout)
     qb = qtensor(b_codes, b_scales, b_fmt, b_grid, layout)
     args = (C.byref(qa), C.byref(qb), m, n, k, _ptr(out), out.stride(0), _stream(stream))
@@ -322,7 +326,7 @@ def prepare_wgrad_gemm(a_codes, a_scales, a_fmt, a_grid, b_codes, b_scales, b_fm
 
     def call():
         _check(entry, fn(*args))
-    call._keep = (qa, qb)
+    call._keep = (qa, qb, a_codes, a_scales, b_codes, b_scales, out)
     return call
 
 
@@ -359,7 +363,8 @@ def rotate(x, axis: int, hadamard_n: int, sign_mask: int = 0, out_dtype=OUT_F32,
 
 
 def prepare_rotate(x, axis: int, hadamard_n: int, sign_mask: int, out_dtype, out, stream=None):
-    """rotate(...) marshalled once into a function of no arguments."""
+    """rotate(...) marshalled once into a function of no arguments that holds
+    x and out."""
     cfg = qconfig(hadamard_n=hadamard_n, sign_mask=sign_mask)
     args = (C.byref(cfg), _ptr(x), x.shape[0], x.shape[1], x.stride(0), axis, out_dtype, _ptr(out),
             out.stride(0), _stream(stream))
@@ -367,7 +372,7 @@ def prepare_rotate(x, axis: int, hadamard_n: int, sign_mask: int, out_dtype, out
 
     def call():
         _check("mxq_rotate", fn(*args))
-    call._keep = cfg
+    call._keep = (cfg, x, out)
     return call
 
 

@@ -218,3 +218,58 @@ def test_rht_sign_mask_is_philox_word0(mxq_lib, orc):
         assert mxq_lib.rht_sign_mask(seed, 32) == w
         assert mxq_lib.rht_sign_mask(seed, 16) == w & 0xFFFF
     assert mxq_lib.rht_sign_mask(7, 8) == 0
+
+
+def test_prepared_calls_hold_their_buffers(mxq_lib):
+    """A prepared call launches later on raw device pointers, so it must keep
+    every tensor it was given alive: a freed buffer would go back to the
+    allocator and could be handed to another tensor (timing loops that
+    rotate several buffer sets would then all touch the same memory).  Only
+    marshalling runs here; nothing is launched."""
+    import gc
+    import types
+    import weakref
+
+    import torch
+    mxq = mxq_lib
+    cfg = mxq.qconfig(hadamard_n=16)
+    st = types.SimpleNamespace(cuda_stream=0)      # a stream handle; nothing is launched
+
+    def alive_after(make):
+        tensors, call = make()
+        refs = [weakref.ref(t) for t in tensors]
+        del tensors
+        gc.collect()
+        assert all(r() is not None for r in refs)
+        del call
+        gc.collect()
+        assert all(r() is None for r in refs)
+
+    def quantize():
+        x = torch.zeros((32, 64), dtype=torch.bfloat16)
+        rc, rs = torch.zeros(32 * 2 * 16, dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8)
+        cc, cs = torch.zeros(64 * 16, dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8)
+        return [x, rc, rs, cc, cs], mxq.prepare_quantize(cfg, x, row=(rc, rs, mxq.FMT_FP4),
+                                                         col=(cc, cs, mxq.FMT_FP4), stream=st)
+
+    def batch():
+        x = torch.zeros((32, 64), dtype=torch.bfloat16)
+        cc, cs = torch.zeros(64 * 16, dtype=torch.uint8), torch.zeros(64, dtype=torch.uint8)
+        return [x, cc, cs], mxq.prepare_quantize_batch([(cfg, x, None, (cc, cs, mxq.FMT_FP4))],
+                                                          stream=st)
+
+    def gemm():
+        ac, as_ = torch.zeros(16 * 4 * 16, dtype=torch.uint8), torch.zeros(16 * 4, dtype=torch.uint8)
+        bc, bs = torch.zeros(16 * 4 * 16, dtype=torch.uint8), torch.zeros(16 * 4, dtype=torch.uint8)
+        out = torch.zeros((16, 16), dtype=torch.float32)
+        return [ac, as_, bc, bs, out], mxq.prepare_wgrad_gemm(
+            ac, as_, mxq.FMT_FP4, mxq.GRID_E2M1, bc, bs, mxq.FMT_FP4, mxq.GRID_E2M1, out,
+            mxq.LAYOUT_ROWS, 16, 16, 128, stream=st)
+
+    def rotate():
+        x = torch.zeros((32, 64), dtype=torch.bfloat16)
+        out = torch.zeros((32, 64), dtype=torch.float32)
+        return [x, out], mxq.prepare_rotate(x, mxq.AXIS_ROW, 16, 0, mxq.OUT_F32, out, stream=st)
+
+    for make in (quantize, batch, gemm, rotate):
+        alive_after(make)
