@@ -600,6 +600,130 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
     }
 }
 
+// Row-wise quantize into the matrix-core layout through LDS: a workgroup takes
+// 16 lines (one 16-line tile) by 32 blocks (8 k-steps), wave w lines 4 w ..
+// 4 w + 3, a lane pair one block as in k_quant_row16.  Written straight to the
+// matrix-core layout, each lane's half block lands in a different 16-byte
+// slot; here the tile's 8 step runs (64 slots each) are assembled in LDS and
+// leave as whole runs of 16-byte nontemporal stores, and the scale words of
+// the tile's 2 groups as whole words.  The LDS image pads each 16-slot row
+// (one block index g of the k-step) and each step so that the 64 lanes of a
+// write land on spread banks (FP4: 272 / 1088 bytes, E2M3: 520 / 2080).
+// Needs rows % 16 == 0, 32 | blocks per row and 16-byte loads (the host checks).
+template <int FMT> struct RowImg {
+    static constexpr int BB = FMT == MXQ_FMT_E2M3 ? 24 : 16;   // bytes per block
+    static constexpr int GP = FMT == MXQ_FMT_E2M3 ? 520 : 272; // bytes per 16-slot row
+    static constexpr int SP = 4 * GP;                           // bytes per step
+};
+
+template <int GRID, int ROUND, int HN, int FMT>
+__global__ __launch_bounds__(256) void k_quant_row16m(const uint16_t *__restrict__ x, uint32_t nbr,
+                                                      int64_t ld, OutDesc out, QKnobs kn)
+{
+    constexpr int BB = RowImg<FMT>::BB, GP = RowImg<FMT>::GP, SP = RowImg<FMT>::SP;
+    constexpr int N = BB / 8;                                    // words per half block
+    __shared__ __align__(16) uint8_t img[8 * SP];
+    __shared__ __align__(16) uint32_t simg[2 * 64];
+    const int t = threadIdx.x, lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int pos = lane & 1, jj = lane >> 1;                    // the lane's block of the 32
+    const uint32_t nbt = nbr / 32;
+    const uint32_t tx = blockIdx.x % nbt, ty = blockIdx.x / nbt; // 32-block chunk, 16-line tile
+    const uint64_t jb = (uint64_t)tx * 32 + jj;
+    const int sl = jj >> 2, g = jj & 3;
+    const float h = kn.sr_bits == 16 ? 0x1p-17f : 0x1p-9f;
+    const float h2 = 2.0f * h;
+    constexpr bool kExact = FMT == MXQ_FMT_E2M3;
+
+    const uint32_t sg = block_signs<HN>(kn, jb) >> (16 * pos);
+    float v[4][16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint64_t line = (uint64_t)ty * 16 + 4 * wv + u;
+        const int64_t off = (int64_t)line * ld + (int64_t)jb * 32 + 16 * pos;
+        const gv4u q0 = *reinterpret_cast<const MXQ_GLOBAL gv4u *>(gmem(x) + off);
+        const gv4u q1 = *reinterpret_cast<const MXQ_GLOBAL gv4u *>(gmem(x) + off + 8);
+        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            v[u][2 * k] = as_f((w[k] << 16) ^ (((sg >> (2 * k)) & 1u) << 31));
+            v[u][2 * k + 1] = as_f((w[k] & 0xFFFF0000u) ^ (((sg >> (2 * k + 1)) & 1u) << 31));
+        }
+    }
+    uint8_t *const sb = reinterpret_cast<uint8_t *>(simg);
+#pragma unroll
+    for (int up = 0; up < 4; up += 2) {
+        uint32_t sc[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const uint64_t line = (uint64_t)ty * 16 + 4 * wv + up + d;
+            sc[d] = col16<GRID, ROUND, HN, kExact>(v[up + d], pos, line * nbr + jb, kn, h, h2);
+        }
+        uint32_t wd[2][N];
+        if constexpr (FMT == MXQ_FMT_E2M3) {
+            f16v s0, s1;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                s0[j] = v[up][2 * j];
+                s1[j] = v[up][2 * j + 1];
+                s0[8 + j] = v[up + 1][2 * j];
+                s1[8 + j] = v[up + 1][2 * j + 1];
+            }
+            uint32_t o[6];
+            cvt_e2m3_32(s0, s1, level_unit<GRID, ROUND>(), o);
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    wd[d][k] = sc[d] == 0xFFu ? 0u : o[3 * d + k];
+        } else {
+#pragma unroll
+            for (int d = 0; d < 2; ++d)
+                pack_fp4<GRID, ROUND>(v[up + d], sc[d], wd[d]);
+        }
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const int l = 4 * wv + up + d;                        // line within the tile
+            uint32_t *dst = reinterpret_cast<uint32_t *>(img + sl * SP + g * GP + l * BB + pos * (BB / 2));
+#pragma unroll
+            for (int k = 0; k < N; ++k)
+                dst[k] = wd[d][k];
+            if (pos == 0)
+                sb[((jj >> 4) * 64 + 16 * g + l) * 4 + (sl & 3)] = (uint8_t)sc[d];
+        }
+    }
+    __syncthreads();
+    // the 8 step runs: run r is step 8 tx + r of tile ty, 64 slots of BB bytes
+    uint8_t *const codes = out.codes;
+    if constexpr (FMT == MXQ_FMT_E2M3) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int q = k * 256 + t, r = q / 96, uu = q - r * 96;   // 16-byte unit uu of run r
+            const int gg = uu / 24, within = (uu - gg * 24) * 16;
+            const uint8_t *src = img + r * SP + gg * GP + within;
+            typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+            const u2v a = *reinterpret_cast<const u2v *>(src);
+            const u2v b = *reinterpret_cast<const u2v *>(src + 8);
+            const gv4u val = {a.x, a.y, b.x, b.y};
+            const uint64_t run = (((uint64_t)tx * 8 + r) * out.ntiles + ty) * 64 * BB;
+            __builtin_nontemporal_store(val, reinterpret_cast<MXQ_GLOBAL gv4u *>(gmem(codes) + run) + uu);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int q = k * 256 + t, r = q >> 6, L = q & 63;
+            const gv4u val = *reinterpret_cast<const gv4u *>(img + r * SP + (L >> 4) * GP + (L & 15) * 16);
+            const uint64_t run = (((uint64_t)tx * 8 + r) * out.ntiles + ty) * 64 * BB;
+            __builtin_nontemporal_store(val, reinterpret_cast<MXQ_GLOBAL gv4u *>(gmem(codes) + run) + L);
+        }
+    }
+    // the scale words of the tile's 2 groups
+    if (t < 128) {
+        const int grp = t >> 6, slot = t & 63;
+        reinterpret_cast<MXQ_GLOBAL uint32_t *>(gmem(out.scales))
+            [(((uint64_t)tx * 2 + grp) * out.ntiles + ty) * 64 + slot] = simg[t];
+    }
+}
+
 // Both outputs from one read.  Phase 1 is k_quant_col's work on the tile
 // (column blocks, 16 rows x 4 columns per lane); each lane also stores its raw
 // bf16 words into an LDS image of the 128 x 128 tile.  After one barrier,
@@ -836,6 +960,17 @@ void launch_dual_hn(int hn, const DualLaunch &q)
 template <int GRID, int ROUND, int HN>
 void launch_row16_fmt(const RowLaunch &q)
 {
+    const uint64_t rows = q.nbr ? q.nblocks / q.nbr : 0;
+    if (q.out.layout == MXQ_LAYOUT_MFMA && q.vec && q.nbr % 32 == 0 && rows % 16 == 0) {
+        const unsigned g = (unsigned)((q.nbr / 32) * (rows / 16));
+        if (q.out.fmt == MXQ_FMT_E2M3)
+            hipLaunchKernelGGL((k_quant_row16m<GRID, ROUND, HN, MXQ_FMT_E2M3>), dim3(g), dim3(256), 0,
+                               q.s, q.x, q.nbr, q.ld, q.out, q.kn);
+        else
+            hipLaunchKernelGGL((k_quant_row16m<GRID, ROUND, HN, MXQ_FMT_FP4>), dim3(g), dim3(256), 0,
+                               q.s, q.x, q.nbr, q.ld, q.out, q.kn);
+        return;
+    }
     const unsigned grid = (unsigned)((q.nblocks + 511) / 512);
     if (q.out.fmt == MXQ_FMT_E2M3)
         hipLaunchKernelGGL((k_quant_row16<GRID, ROUND, HN, MXQ_FMT_E2M3>), dim3(grid), dim3(256),

@@ -174,7 +174,8 @@ def test_full_size_workloads_whole(orc, case):
 
 @pytest.mark.parametrize("shape,row,col", [((96, 256), True, False), ((256, 100), False, True),
                                            ((128, 384), True, True), ((40, 128), True, False),
-                                           ((640, 72), False, True)])
+                                           ((640, 72), False, True), ((16, 1024), True, False),
+                                           ((48, 3072), True, False), ((32, 1152), True, False)])
 @pytest.mark.parametrize("knobs", [(0, 0, 16), (1, 1, 32), (1, 0, 0)], ids=_knob_id)
 def test_mfma_layout_outputs(orc, shape, row, col, knobs):
     """Outputs in the matrix-core operand layout equal the oracle's row-layout
