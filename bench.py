@@ -772,10 +772,11 @@ def workloads_report(torch, mxq, synth, dev, reps, only=None):
         x0 = torch.from_numpy(x_np.view(np.int16)).to(dev).view(torch.bfloat16)
         for i in range(n_sets(nbytes)):
             x = x0 if i == 0 else x0.clone()
-            r = mxq.empty_qtensor(rows, cols, case.fmt, dev) if case.row_out else None
-            c = mxq.empty_qtensor(cols, rows, case.fmt, dev) if case.col_out else None
-            calls.append(mxq.prepare_quantize(cfg, x, row=(r[0], r[1], case.fmt) if r else None,
-                                              col=(c[0], c[1], case.fmt) if c else None))
+            lay = case.layout
+            r = mxq.empty_qtensor(rows, cols, case.fmt, dev, lay) if case.row_out else None
+            c = mxq.empty_qtensor(cols, rows, case.fmt, dev, lay) if case.col_out else None
+            calls.append(mxq.prepare_quantize(cfg, x, row=(r[0], r[1], case.fmt, lay) if r else None,
+                                              col=(c[0], c[1], case.fmt, lay) if c else None))
         for c in calls:
             c()
         torch.cuda.synchronize()

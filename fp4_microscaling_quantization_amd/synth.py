@@ -17,6 +17,7 @@ import numpy as np
 GRID_E2M1, GRID_E1M2, GRID_E2M1_MAX4, GRID_E2M1_MAX3 = 0, 1, 2, 3
 RTNE, SR = 0, 1
 FMT_FP4, FMT_E2M3 = 0, 1
+LAYOUT_ROWS, LAYOUT_MFMA = 0, 1
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -95,6 +96,7 @@ class QuantCase:
     sr_bits: int = 16
     sign_mode: int = 0                # 0: one mask for every block; 1: drawn per block
     sign_seed: int = 0
+    layout: int = LAYOUT_ROWS         # of every output: row layout or the matrix-core layout
     extra: dict = field(default_factory=dict)
 
     def knobs(self) -> dict:
@@ -149,7 +151,8 @@ SR_SEED_WGRAD = 7
 
 def workload_cases() -> list[QuantCase]:
     """The quantize calls of the five workloads at full size, plus the
-    range-restricted E2M1 grid and per-block signs on the same tensors."""
+    range-restricted E2M1 grid and per-block signs on the same tensors, and
+    the layer's Fprop / Dgrad operands in the matrix-core layout."""
     return [
         QuantCase("x1024_e2m1_rtne", 1024, 1024, x_1024),
         QuantCase("x8192_h16_e2m1", 8192, 4096, x_8192x4096, hadamard_n=16),
@@ -179,4 +182,14 @@ def workload_cases() -> list[QuantCase]:
         QuantCase("wgrad_dy_rht16_e1m2_sr8_col_e2m3", 8192, 4096, dy_8192x4096, grid=GRID_E1M2,
                   round=SR, hadamard_n=16, sign_mask=sign_mask(SIGNS_WGRAD, 16), row_out=False,
                   col_out=True, fmt=FMT_E2M3, sr_seed=SR_SEED_WGRAD, sr_bits=8),
+        # the operands of the layer's other two products, written straight into
+        # the matrix-core layout: Fprop takes X and W row-wise, Dgrad dY row-wise
+        # and W column-wise
+        QuantCase("fprop_x8192_rht32_e2m1_row_mfma", 8192, 4096, x_8192x4096, hadamard_n=32,
+                  sign_mask=sign_mask(SIGNS_W, 32), layout=LAYOUT_MFMA),
+        QuantCase("w14336_rht32_e2m1_dual_mfma", 14336, 4096, w_14336x4096, hadamard_n=32,
+                  sign_mask=sign_mask(SIGNS_W, 32), col_out=True, layout=LAYOUT_MFMA),
+        QuantCase("dgrad_dy8192x14336_rht32_e2m1_sr_row_mfma", 8192, 14336, dy_8192x14336,
+                  round=SR, hadamard_n=32, sign_mask=sign_mask(SIGNS_W, 32), sr_seed=11,
+                  layout=LAYOUT_MFMA),
     ]

@@ -160,12 +160,14 @@ def test_full_size_workloads_whole(orc, case):
     say("full", case.name, x.shape)
     xt = to_dev_bf16(x)
     q = mxq.quantize(xt, row=case.row_out, col=case.col_out, row_fmt=case.fmt, col_fmt=case.fmt,
-                     **case.knobs())
+                     row_layout=case.layout, col_layout=case.layout, **case.knobs())
     p = orc.qparams(**case.knobs())
     for axis, key in ((orc.AXIS_ROW, "row"), (orc.AXIS_COL, "col")):
         if key not in q:
             continue
         c, s = oracle_par.quantize(orc, x, axis, p, case.fmt)
+        if case.layout == synth.LAYOUT_MFMA:
+            c, s = orc.to_mfma_layout(c, s, case.fmt)
         gs = host(q[key][1])
         assert np.array_equal(gs, s), (key, "scales", np.argwhere(gs != s)[:4].tolist())
         gc = host(q[key][0])
