@@ -600,16 +600,19 @@ __global__ __launch_bounds__(256) void k_quant_row16(const uint16_t *__restrict_
     }
 }
 
-// Row-wise quantize into the matrix-core layout through LDS: a workgroup takes
-// 16 lines (one 16-line tile) by 32 blocks (8 k-steps), wave w lines 4 w ..
+// Row-wise quantize through LDS: a workgroup takes 16 lines (one 16-line tile
+// of the matrix-core layout) by 32 blocks (8 k-steps), wave w lines 4 w ..
 // 4 w + 3, a lane pair one block as in k_quant_row16.  Written straight to the
 // matrix-core layout, each lane's half block lands in a different 16-byte
 // slot; here the tile's 8 step runs (64 slots each) are assembled in LDS and
 // leave as whole runs of 16-byte nontemporal stores, and the scale words of
-// the tile's 2 groups as whole words.  The LDS image pads each 16-slot row
-// (one block index g of the k-step) and each step so that the 64 lanes of a
-// write land on spread banks (FP4: 272 / 1088 bytes, E2M3: 520 / 2080).
-// Needs rows % 16 == 0, 32 | blocks per row and 16-byte loads (the host checks).
+// the tile's 2 groups as whole words.  In the row layout the same image
+// leaves as 16 line runs of 32 blocks (512 or 768 bytes) and 16 runs of 32
+// scale bytes.  The LDS image pads each 16-slot row (one block index g of the
+// k-step) and each step so that the 64 lanes of a write land on spread banks
+// (FP4: 272 / 1088 bytes, E2M3: 520 / 2080).  Needs rows % 16 == 0, 32 |
+// blocks per row and 16-byte loads; in the row layout also 16-byte aligned
+// codes and 4-byte aligned scales (the host checks).
 template <int FMT> struct RowImg {
     static constexpr int BB = FMT == MXQ_FMT_E2M3 ? 24 : 16;   // bytes per block
     static constexpr int GP = FMT == MXQ_FMT_E2M3 ? 520 : 272; // bytes per 16-slot row
@@ -630,6 +633,7 @@ __global__ __launch_bounds__(256) void k_quant_row16m(const uint16_t *__restrict
     const uint32_t tx = blockIdx.x % nbt, ty = blockIdx.x / nbt; // 32-block chunk, 16-line tile
     const uint64_t jb = (uint64_t)tx * 32 + jj;
     const int sl = jj >> 2, g = jj & 3;
+    const bool rowl = out.layout == MXQ_LAYOUT_ROWS;
     const float h = kn.sr_bits == 16 ? 0x1p-17f : 0x1p-9f;
     const float h2 = 2.0f * h;
     constexpr bool kExact = FMT == MXQ_FMT_E2M3;
@@ -688,10 +692,42 @@ __global__ __launch_bounds__(256) void k_quant_row16m(const uint16_t *__restrict
             for (int k = 0; k < N; ++k)
                 dst[k] = wd[d][k];
             if (pos == 0)
-                sb[((jj >> 4) * 64 + 16 * g + l) * 4 + (sl & 3)] = (uint8_t)sc[d];
+                sb[rowl ? l * 32 + jj : ((jj >> 4) * 64 + 16 * g + l) * 4 + (sl & 3)] = (uint8_t)sc[d];
         }
     }
     __syncthreads();
+    if (rowl) {
+        // line runs: 16-byte unit u of line l (FP4: block u; E2M3: 8-byte
+        // chunks 2 u and 2 u + 1, chunk c being bytes 8 (c % 3) of block c / 3)
+        constexpr int U = 2 * BB;                                  // units per line run
+        MXQ_GLOBAL uint8_t *const codes = gmem(out.codes);
+#pragma unroll
+        for (int k = 0; k < U / 16; ++k) {
+            const int q = k * 256 + t, l = q / U, u = q - l * U;
+            gv4u val;
+            if constexpr (FMT == MXQ_FMT_E2M3) {
+                typedef uint32_t u2v __attribute__((ext_vector_type(2)));
+                u2v w2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int c = 2 * u + e, b = c / 3;
+                    w2[e] = *reinterpret_cast<const u2v *>(img + (b >> 2) * SP + (b & 3) * GP + l * BB +
+                                                           (c - 3 * b) * 8);
+                }
+                val = gv4u{w2[0].x, w2[0].y, w2[1].x, w2[1].y};
+            } else {
+                val = *reinterpret_cast<const gv4u *>(img + (u >> 2) * SP + (u & 3) * GP + l * BB);
+            }
+            const uint64_t run = (((uint64_t)ty * 16 + l) * out.nbk + (uint64_t)tx * 32) * BB;
+            __builtin_nontemporal_store(val, reinterpret_cast<MXQ_GLOBAL gv4u *>(codes + run) + u);
+        }
+        if (t < 128) {
+            const int l = t >> 3, w = t & 7;
+            reinterpret_cast<MXQ_GLOBAL uint32_t *>(
+                gmem(out.scales) + ((uint64_t)ty * 16 + l) * out.nbk + (uint64_t)tx * 32)[w] = simg[t];
+        }
+        return;
+    }
     // the 8 step runs: run r is step 8 tx + r of tile ty, 64 slots of BB bytes
     uint8_t *const codes = out.codes;
     if constexpr (FMT == MXQ_FMT_E2M3) {
@@ -961,7 +997,10 @@ template <int GRID, int ROUND, int HN>
 void launch_row16_fmt(const RowLaunch &q)
 {
     const uint64_t rows = q.nbr ? q.nblocks / q.nbr : 0;
-    if (q.out.layout == MXQ_LAYOUT_MFMA && q.vec && q.nbr % 32 == 0 && rows % 16 == 0) {
+    const bool out_ok = q.out.layout == MXQ_LAYOUT_MFMA ||
+                        (reinterpret_cast<uintptr_t>(q.out.codes) % 16 == 0 &&
+                         reinterpret_cast<uintptr_t>(q.out.scales) % 4 == 0);
+    if (out_ok && q.vec && q.nbr % 32 == 0 && rows % 16 == 0 && rows > 0) {
         const unsigned g = (unsigned)((q.nbr / 32) * (rows / 16));
         if (q.out.fmt == MXQ_FMT_E2M3)
             hipLaunchKernelGGL((k_quant_row16m<GRID, ROUND, HN, MXQ_FMT_E2M3>), dim3(g), dim3(256), 0,

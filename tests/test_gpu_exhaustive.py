@@ -91,12 +91,16 @@ def test_every_bf16_pattern_every_kernel(orc, mxq_lib, gname, rnd, fmt, layout):
     _eq(host(q[1]), R[1], "column kernel scales")
     _eq(host(q[0]), R[0], "column kernel codes")
 
-    # the row kernel into the matrix-core layout, on the same blocks as lines of
-    # 32 blocks (whole 16-line tiles: the kernel that stages a tile in LDS)
+    # the row kernel on the same blocks as lines of 32 blocks (whole 16-line
+    # tiles: the kernel that stages a tile in LDS), into both layouts
     x2 = x.reshape(x.shape[0] // 2, 2 * x.shape[1])
+    x2d = to_dev_bf16(x2)
     R4 = oracle_par.quantize(orc, x2, orc.AXIS_ROW, p, fmt)
+    q = mxq.quantize(x2d, row=True, col=False, row_fmt=fmt, **kn)["row"]
+    _eq(host(q[1]), R4[1], "row kernel (32-block lines) scales")
+    _eq(host(q[0]), R4[0], "row kernel (32-block lines) codes")
     tc, ts = orc.to_mfma_layout(R4[0], R4[1], fmt, fill=0xA5)
-    q = mxq.quantize(to_dev_bf16(x2), row=True, col=False, row_fmt=fmt,
+    q = mxq.quantize(x2d, row=True, col=False, row_fmt=fmt,
                      row_layout=mxq.LAYOUT_MFMA, fill=0xA5, **kn)["row"]
     _eq(host(q[1]), ts, "row kernel (matrix-core layout) scales")
     _eq(host(q[0]), tc, "row kernel (matrix-core layout) codes")

@@ -174,6 +174,35 @@ def test_full_size_workloads_whole(orc, case):
         assert np.array_equal(gc, c), (key, "codes", np.argwhere(gc != c)[:4].tolist())
 
 
+@pytest.mark.parametrize("shape", [(32, 1024), (48, 3072)])
+@pytest.mark.parametrize("fmt", [0, 1], ids=["fp4", "e2m3"])
+def test_row_layout_output_offsets(orc, shape, fmt):
+    """Row-layout outputs that start at any allowed offset (codes 4-byte
+    aligned, scales at any byte) hold the oracle's bytes, and the bytes around
+    them stay untouched: whole 16-line tiles of 32 blocks take the staged
+    kernel when codes are 16-byte and scales 4-byte aligned, the per-lane
+    kernel otherwise."""
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    rows, cols = shape
+    x = synth.normal_outlier_channels(rows, cols, seed=cols, ch_seed=rows, frac=0.03)
+    kw = _params(orc, 0, 1, 32, seed=6)
+    p = orc.qparams(**kw)
+    c, s = orc.quantize(x, orc.AXIS_ROW, p, fmt)
+    xt = to_dev_bf16(x)
+    cbytes, sbytes = c.size, s.size
+    for co, so in ((0, 0), (4, 0), (8, 0), (0, 1), (0, 2), (4, 4)):
+        say("row offsets", shape, fmt, co, so)
+        cbuf = torch.full((cbytes + 64,), 0x5A, dtype=torch.uint8, device=dev())
+        sbuf = torch.full((sbytes + 64,), 0x5A, dtype=torch.uint8, device=dev())
+        mxq.quantize_into(mxq.qconfig(**kw), xt, row=(cbuf[co:co + cbytes], sbuf[so:so + sbytes], fmt))
+        gc, gs = host(cbuf), host(sbuf)
+        assert np.array_equal(gc[co:co + cbytes], c.reshape(-1)), (co, so, "codes")
+        assert np.array_equal(gs[so:so + sbytes], s.reshape(-1)), (co, so, "scales")
+        assert (np.delete(gc, np.arange(co, co + cbytes)) == 0x5A).all(), (co, so, "codes guard")
+        assert (np.delete(gs, np.arange(so, so + sbytes)) == 0x5A).all(), (co, so, "scales guard")
+
+
 @pytest.mark.parametrize("shape,row,col", [((96, 256), True, False), ((256, 100), False, True),
                                            ((128, 384), True, True), ((40, 128), True, False),
                                            ((640, 72), False, True), ((16, 1024), True, False),
