@@ -203,6 +203,42 @@ def test_row_layout_output_offsets(orc, shape, fmt):
         assert (np.delete(gs, np.arange(so, so + sbytes)) == 0x5A).all(), (co, so, "scales guard")
 
 
+@pytest.mark.parametrize("shape", [(96, 256), (256, 384)])
+@pytest.mark.parametrize("fmt", [0, 1], ids=["fp4", "e2m3"])
+@pytest.mark.parametrize("dual", [False, True], ids=["col", "dual"])
+def test_col_layout_output_offsets(orc, shape, fmt, dual):
+    """Column-wise row-layout outputs (alone or beside the row output) at
+    codes offsets 0/4/8 and scale offsets 0/1: full tiles leave their column
+    runs in 16-byte stores when the codes are 16-byte aligned (E2M3: with an
+    even block count per line; 96 rows have an odd one), in word stores
+    otherwise; bytes around the outputs stay untouched."""
+    import torch
+    from fp4_microscaling_quantization_amd import mxq
+    rows, cols = shape
+    x = synth.normal_outlier_channels(rows, cols, seed=rows + 1, ch_seed=cols + 1, frac=0.03)
+    kw = _params(orc, 1, 1, 16, seed=7)
+    p = orc.qparams(**kw)
+    want = {"col": orc.quantize(x, orc.AXIS_COL, p, fmt)}
+    if dual:
+        want["row"] = orc.quantize(x, orc.AXIS_ROW, p, 1 - fmt)
+    xt = to_dev_bf16(x)
+    for co, so in ((0, 0), (4, 0), (8, 1), (0, 1)):
+        say("col offsets", shape, fmt, dual, co, so)
+        bufs = {}
+        for key, (c, s) in want.items():
+            bufs[key] = (torch.full((c.size + 64,), 0x5A, dtype=torch.uint8, device=dev()),
+                         torch.full((s.size + 64,), 0x5A, dtype=torch.uint8, device=dev()))
+        outs = {key: (cb[co:co + want[key][0].size], sb[so:so + want[key][1].size],
+                      fmt if key == "col" else 1 - fmt) for key, (cb, sb) in bufs.items()}
+        mxq.quantize_into(mxq.qconfig(**kw), xt, row=outs.get("row"), col=outs["col"])
+        for key, (c, s) in want.items():
+            gc, gs = host(bufs[key][0]), host(bufs[key][1])
+            assert np.array_equal(gc[co:co + c.size], c.reshape(-1)), (key, co, so, "codes")
+            assert np.array_equal(gs[so:so + s.size], s.reshape(-1)), (key, co, so, "scales")
+            assert (np.delete(gc, np.arange(co, co + c.size)) == 0x5A).all(), (key, co, so)
+            assert (np.delete(gs, np.arange(so, so + s.size)) == 0x5A).all(), (key, co, so)
+
+
 @pytest.mark.parametrize("shape,row,col", [((96, 256), True, False), ((256, 100), False, True),
                                            ((128, 384), True, True), ((40, 128), True, False),
                                            ((640, 72), False, True), ((16, 1024), True, False),
