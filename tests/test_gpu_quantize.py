@@ -54,9 +54,11 @@ def _check(orc, x, knobs, row_fmt=None, col_fmt=None, ld=None, tag=""):
         assert np.array_equal(gc, c), f"col codes differ at {np.argwhere(gc != c)[:5]}"
 
 
-@pytest.mark.parametrize("shape", [(77, 96), (33, 4128), (1, 32), (256, 512)])
+@pytest.mark.parametrize("shape", [(77, 96), (33, 4128), (1, 32), (256, 512), (64, 1024),
+                                   (48, 2048)])
 @pytest.mark.parametrize("knobs", KNOBS, ids=_knob_id)
 def test_row_parity(orc, shape, knobs):
+    # (64, 1024) and (48, 2048): whole 16-line tiles of 32 blocks, the staged kernel
     x = synth.normal_outlier_channels(*shape, seed=shape[0], ch_seed=shape[1], frac=0.05)
     for fmt in (0, 1):
         _check(orc, x, _params(orc, *knobs, seed=shape[0]), row_fmt=fmt, tag="row")
