@@ -126,6 +126,12 @@ def test_padded_leading_dimension(orc, knobs):
     _check(orc, x, p, row_fmt=0, ld=104, tag="ld-row")
     _check(orc, x, p, col_fmt=0, ld=136, tag="ld-col")
     _check(orc, x, p, row_fmt=0, col_fmt=1, ld=128, tag="ld-dual")
+    # a whole 16-line tile of 32 blocks (the staged row kernel) and full
+    # 128 x 128 tiles (staged column and dual outputs) with padded rows
+    x2 = synth.normal(32, 1024, seed=5)
+    _check(orc, x2, p, row_fmt=1, ld=1040, tag="ld-row-staged")
+    _check(orc, x2, p, col_fmt=1, ld=1032, tag="ld-col-staged")
+    _check(orc, x2, p, row_fmt=1, col_fmt=0, ld=1096, tag="ld-dual-staged")
 
 
 def test_sr_8_bit_stream(orc):
