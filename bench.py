@@ -196,6 +196,11 @@ def parse():
     ap.add_argument("--workloads-only", default=None, metavar="NAMES",
                     help="time only these workload quantize calls (comma-separated case "
                          "names, or 'all') and print their JSON object; for counter runs")
+    ap.add_argument("--stats-only", action="store_true",
+                    help="time only the bias statistics calls and print their JSON object; "
+                         "for counter runs")
+    ap.add_argument("--no-stats", action="store_true",
+                    help="skip the timing of the bias statistics calls")
     ap.add_argument("--no-other-form", action="store_true",
                     help="skip the GEMM timed with the other operand form")
     ap.add_argument("--no-sr8", action="store_true",
@@ -226,6 +231,11 @@ def main():
             copy_calibration(torch, dev)
         rep = workloads_report(torch, mxq, synth, dev, max(args.steps, 10), only)
         print(json.dumps({"workloads": rep}), flush=True)
+        return
+
+    if args.stats_only:
+        print(json.dumps({"stats": stats_report(torch, mxq, synth, dev, max(args.steps, 10))}),
+              flush=True)
         return
 
     grid = mxq.GRID_E1M2 if args.variant == "e1m2" else mxq.GRID_E2M1
@@ -423,6 +433,8 @@ def main():
     if not args.no_workloads:
         rec["workloads"] = workloads_report(torch, mxq, synth, dev, max(args.steps, 10))
 
+    if not args.no_stats:
+        rec["stats"] = stats_report(torch, mxq, synth, dev, max(args.steps, 10))
     if not args.no_layer_gemms:
         rec["layer_gemms"] = layer_gemms_report(torch, mxq, synth, dev, grid, fmt,
                                                 max(args.steps, 10), mfma_peak)
@@ -791,6 +803,49 @@ def workloads_report(torch, mxq, synth, dev, reps, only=None):
         out[case.name] = {"sets": len(calls), "avg_us": round(t * 1e6, 2),
                           "GBps": round(nbytes / t / 1e9, 1),
                           "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del calls
+        torch.cuda.empty_cache()
+    return out
+
+
+def stats_report(torch, mxq, synth, dev, reps):
+    """The bias statistics (mxq_bias_stats: rotate, dequantize and the fp64
+    sums against the codes of one quantize) of the 8192 x 4096 activation, H16,
+    E2M1, FP4 codes, along rows and along columns: `reps` back-to-back calls
+    over rotating sets (input, codes, scales) that span more than the
+    last-level cache.  Algorithmic bytes per call: 2 B read per element plus
+    the 0.5 B of codes and 1/32 B of scale read back."""
+    import numpy as np
+    rows, cols = 8192, 4096
+    kn = dict(grid=mxq.GRID_E2M1, hadamard_n=16)
+    x0 = torch.from_numpy(synth.x_8192x4096().view(np.int16)).to(dev).view(torch.bfloat16)
+    nbytes = rows * cols * (2.0 + 0.5 + 1.0 / 32)
+    out = {}
+    s = torch.cuda.current_stream()
+    for axis, name in ((0, "x8192_h16_e2m1_row"), (1, "x8192_h16_e2m1_col")):
+        key = "row" if axis == 0 else "col"
+        wsb = mxq.lib().mxq_bias_stats_workspace_size(rows, cols, axis)
+        calls = []
+        for i in range(n_sets(nbytes)):
+            x = x0 if i == 0 else x0.clone()
+            q = mxq.quantize(x, row=axis == 0, col=axis == 1, **kn)[key]
+            st = torch.zeros(256, dtype=torch.uint8, device=dev)
+            ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device=dev)
+            calls.append(mxq.prepare_bias_stats(x, axis, q[0], q[1], mxq.FMT_FP4, st, ws, **kn))
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
+        time.sleep(0.05)
+        e0, e1 = HipEvent(), HipEvent()
+        e0.record(s)
+        for i in range(reps):
+            calls[i % len(calls)]()
+        e1.record(s)
+        torch.cuda.synchronize()
+        t = e0.elapsed_ms(e1) * 1e-3 / reps
+        out[name] = {"sets": len(calls), "avg_us": round(t * 1e6, 2),
+                     "GBps": round(nbytes / t / 1e9, 1),
+                     "frac_hbm": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
         del calls
         torch.cuda.empty_cache()
     return out

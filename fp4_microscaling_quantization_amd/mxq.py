@@ -398,6 +398,27 @@ def bias_stats(x, axis: int, codes, scales, fmt: int, grid=GRID_E2M1, round=RTNE
     return _stats_dict(out)
 
 
+def prepare_bias_stats(x, axis: int, codes, scales, fmt: int, out, ws, grid=GRID_E2M1,
+                       round=RTNE, hadamard_n=0, sign_mask=0, sr_seed=0, sr_stream=0,
+                       sr_bits=16, stream=None, sign_mode=SIGNS_MASK, sign_seed=0):
+    """bias_stats(...) marshalled once into a function of no arguments that
+    holds every tensor it was given: `out` is a device byte tensor of
+    sizeof(mxq_stats), `ws` one of at least mxq_bias_stats_workspace_size
+    bytes.  The call leaves the statistics in `out` (no host copy)."""
+    cfg = qconfig(grid, round, hadamard_n, sign_mask, sr_seed, sr_stream, sr_bits, sign_mode,
+                  sign_seed)
+    rows, cols = x.shape
+    q = qtensor(codes, scales, fmt, grid)
+    args = (C.byref(cfg), _ptr(x), rows, cols, x.stride(0), axis, C.byref(q), _ptr(out),
+            _ptr(ws), ws.numel(), _stream(stream))
+    fn = lib().mxq_bias_stats
+
+    def call():
+        _check("mxq_bias_stats", fn(*args))
+    call._keep = (cfg, q, x, codes, scales, out, ws)
+    return call
+
+
 def _stats_dict(out) -> dict:
     """The mxq_stats a call wrote into the device byte tensor `out`."""
     st = Stats.from_buffer_copy(bytes(out.cpu().numpy().tobytes()))
