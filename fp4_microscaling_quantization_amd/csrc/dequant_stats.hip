@@ -1,6 +1,7 @@
 // Reconstruction (mxq_dequantize) and the shrinkage-bias / SQNR statistics
 // (mxq_bias_stats) of block-quantized tensors.  Support kernels of the
-// quantizer: memory-bound, one pass, no tuning beyond coalesced access.
+// quantizer, one pass each: the reconstruction is memory-bound; the
+// statistics are bound by their fp64 terms.
 //
 // Reconstruction yhat = (-1)^s G_m 2^e follows the shared-exponent format of
 // the htx.com news "Pretraining large language models with MXFP4", section
@@ -258,6 +259,9 @@ __device__ __forceinline__ void stat_block(StatAcc &acc, const float (&y)[32], u
         hist_hi += m < 4u ? 0u : inc;
     }
     acc.u[0] += 32;
+    // the block's count as one 32-bit value (left to itself the compiler adds
+    // each element's 0 or 1 straight into the 64-bit sum)
+    asm volatile("" : "+v"(nsat));
     acc.u[1] += nsat;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
